@@ -1,0 +1,282 @@
+/*
+ * amk.h: C ABI of the MI355X persistent decode megakernel.
+ *
+ * The library runs one batch-1 autoregressive decode step of a Llama-style
+ * decoder as ONE persistent cooperative HIP launch: one workgroup per queue
+ * (one queue per compute unit), each walking its slice of a topologically
+ * ordered task DAG with wait -> dispatch -> signal on monotonic counters.
+ * This is the design the AutoMegaKernel summary pages describe ("AutoMegaKernel
+ * (AMK)" technical summary, section "Methodology": layer 0 is a persistent
+ * kernel with one cooperative block per multiprocessor and a local queue per
+ * block over a global topological order, synchronised by monotonic counters
+ * without locks; layer 1 holds the GEMV / attention / RMSNorm micro-kernels;
+ * layer 2 lowers the model to a typed Schedule IR configured by a
+ * ScheduleConfig with tiling, fusion, SM assignment and pipelining depth).
+ * The problem it addresses is the one in that page's section "Problem
+ * statement": single-stream batch-1 decode is bound by HBM bandwidth, with a
+ * latency floor of weight bytes over bandwidth.
+ *
+ * Conventions (all entry points):
+ *   - plain C types only; no exception crosses the ABI; every call that can
+ *     fail returns amk_status and leaves a message in amk_last_error();
+ *   - "host" pointers are CPU memory, "device" pointers are HIP device memory
+ *     on the current device; the caller owns every buffer it passes in;
+ *   - the library owns the opaque handles it returns and frees them in the
+ *     matching *_free / *_destroy call.
+ */
+#ifndef AMK_H
+#define AMK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AMK_OK = 0,
+  AMK_ERR_INVALID_ARG = -1,      /* null pointer, bad size, gap in positions */
+  AMK_ERR_UNSUPPORTED = -2,      /* model or schedule variant not supported */
+  AMK_ERR_UNSAFE_SCHEDULE = -3,  /* the static safety gate rejected it */
+  AMK_ERR_OUT_OF_RANGE = -4,     /* token / position / id out of range */
+  AMK_ERR_HIP = -5,              /* a HIP runtime call failed */
+  AMK_ERR_NOMEM = -6,            /* host or device allocation failed */
+  AMK_ERR_TIMEOUT = -7           /* a device-side wait exceeded its budget */
+} amk_status;
+
+/* Weight storage formats ("Quantised megakernels" contribution of the AMK
+ * summary: int8 and int4 weight-only kernels from the same IR path). */
+typedef enum {
+  AMK_W_BF16 = 0,       /* bf16 [out][in] */
+  AMK_W_INT8_ROW = 1,   /* int8, one fp32 scale per output row */
+  AMK_W_INT4_G128 = 2   /* int4, groups of 128 inputs, fp16 scale + fp16 zero */
+} amk_wfmt;
+
+/* Llama-family decoder shape.  Biased projections are not supported
+ * (the AMK summary's "Automatic generation coverage" contribution: variants
+ * with biased projections are rejected): attn_bias / mlp_bias must be 0, else
+ * amk_build_schedule returns AMK_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, max_ctx;
+  float rms_eps, rope_theta;
+  int32_t tied_embeddings; /* lm_head = token embedding */
+  int32_t attn_bias, mlp_bias;
+  int32_t wfmt;            /* amk_wfmt of the 7 projections per layer and lm_head */
+  int32_t act_bf16;        /* 1: round every projection input vector to bf16 */
+} amk_model_config;
+
+/* The ScheduleConfig (AMK summary, "Methodology", layer 2): tiling, fusion,
+ * compute-unit assignment and pipelining depth.  0 in a tiles_* / attn_splits
+ * field means "automatic".  Tiles are tasks per phase; rows per task follow
+ * (an even split of the phase's output rows). */
+typedef struct {
+  int32_t num_cus;         /* queues = workgroups of the persistent launch */
+  int32_t wg_threads;      /* threads per workgroup: 512 */
+  int32_t tiles_qkv, tiles_o, tiles_gateup, tiles_down, tiles_lm;
+  int32_t attn_splits;     /* position splits per kv head (log-sum-exp merged) */
+  int32_t cu_policy;       /* 0: task i of T -> queue i*num_cus/T; 1: i % num_cus */
+  int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16 */
+  uint32_t fuse_flags;     /* AMK_FUSE_* bits; only AMK_FUSE_DEFAULT is built */
+} amk_schedule_config;
+
+#define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */
+#define AMK_FUSE_ROPE_KV 0x2u        /* RoPE + KV append in the QKV task */
+#define AMK_FUSE_SWIGLU 0x4u         /* silu(gate)*up in the gate/up task */
+#define AMK_FUSE_RESIDUAL 0x8u       /* residual add in the O / down epilogue */
+#define AMK_FUSE_DEFAULT 0xFu
+
+/* ---- Schedule IR, flat view ------------------------------------------- */
+
+typedef enum {
+  AMK_TASK_NOP = 0,     /* waits and signals only; accesses as declared */
+  AMK_TASK_QKV = 1,     /* p: layer, unit0, unit1 (rope pair units) */
+  AMK_TASK_ATTN = 2,    /* p: layer, kv head, split, n_splits */
+  AMK_TASK_MERGE = 3,   /* p: layer, q head, n_splits */
+  AMK_TASK_OPROJ = 4,   /* p: layer, row0, row1 */
+  AMK_TASK_GATEUP = 5,  /* p: layer, j0, j1 */
+  AMK_TASK_DOWN = 6,    /* p: layer, row0, row1 */
+  AMK_TASK_LMHEAD = 7,  /* p: row0, row1 */
+  AMK_TASK_NTYPES = 8
+} amk_task_type;
+
+typedef enum {
+  AMK_BUF_WEIGHT = 0,   /* read-only input */
+  AMK_BUF_SCRATCH = 1,  /* activations inside one step */
+  AMK_BUF_OUTPUT = 2,   /* logits */
+  AMK_BUF_STATE = 3,    /* KV row written at this step's position */
+  AMK_BUF_HISTORY = 4   /* KV rows before this step's position (read-only) */
+} amk_buffer_kind;
+
+#define AMK_ACCESS_READ 1
+#define AMK_ACCESS_WRITE 2
+
+typedef struct { int32_t type, cu; int32_t p[8]; } amk_task_desc;
+typedef struct { int32_t counter; uint32_t threshold; } amk_wait_desc;
+typedef struct { int32_t buffer, mode; int64_t begin, end; } amk_access_desc; /* bytes [begin,end) */
+typedef struct { int64_t size; int32_t kind; int32_t reserved; } amk_buffer_desc;
+
+/* Flat, caller-readable view of a schedule.  CSR arrays: the waits of task i
+ * are waits[wait_off[i] .. wait_off[i+1]), likewise signals and accesses;
+ * queue c is queue[queue_off[c] .. queue_off[c+1]) in execution order. */
+typedef struct {
+  amk_model_config model;
+  amk_schedule_config config;
+  int32_t n_tasks, n_counters, n_buffers, n_cus;
+  const amk_task_desc* tasks;
+  const int32_t* wait_off; const amk_wait_desc* waits;
+  const int32_t* sig_off;  const int32_t* sigs;
+  const int32_t* acc_off;  const amk_access_desc* accesses;
+  const int32_t* queue_off; const int32_t* queue;
+  const amk_buffer_desc* buffers;
+} amk_schedule_desc;
+
+typedef struct amk_schedule amk_schedule;   /* opaque, host only */
+typedef struct amk_engine amk_engine;       /* opaque, binds a schedule to device memory */
+
+/* Validator verdict (AMK summary, "Methodology", the safety gate: deadlock
+ * freedom = acyclic producer/consumer DAG, satisfiable thresholds
+ * 1 <= t <= #producers, valid per-SM queue orders; race freedom = shared
+ * multi-producer counters fully joined before a consumer waits, memory
+ * accesses ordered by happens-before; correctness = output reachability and
+ * referential integrity).  code 0 = safe, else the first failing rule:
+ *   1 REF, 2 THRESHOLD, 3 CYCLE, 4 QUEUE_ORDER, 5 UNDER_JOINED, 6 RACE,
+ *   7 OUTPUT.  task / counter / aux name the smallest offender (-1 if none;
+ *   for RACE, task < aux is the racing pair; for OUTPUT with task -1, aux is
+ *   the buffer that is not fully written). */
+typedef struct { int32_t code, task, counter, aux; } amk_verdict;
+
+enum { AMK_V_OK = 0, AMK_V_REF = 1, AMK_V_THRESHOLD = 2, AMK_V_CYCLE = 3, AMK_V_QUEUE_ORDER = 4,
+       AMK_V_UNDER_JOINED = 5, AMK_V_RACE = 6, AMK_V_OUTPUT = 7 };
+
+/* Device buffers, all owned by the caller.  weights[k] is the packed tensor k
+ * (k < amk_packed_count), written with amk_pack_tensor and copied to the
+ * device; kv_cache holds amk_kv_bytes bytes laid out
+ * [n_layers][2 (K,V)][n_kv_heads][max_ctx][head_dim] bf16; logits holds
+ * vocab fp32 values. */
+typedef struct {
+  const void* const* weights;
+  int32_t n_weights;
+  void* kv_cache;
+  float* logits;
+} amk_device_buffers;
+
+/* ---- configuration ------------------------------------------------------ */
+
+/* Default ScheduleConfig for a model on a device with device_cus compute
+ * units (one queue per CU). */
+amk_status amk_default_schedule_config(const amk_model_config* model, int32_t device_cus,
+                                       amk_schedule_config* out);
+
+/* ---- lowering and the safety gate ---------------------------------------- */
+
+/* Lower the model to a typed Schedule DAG (AMK summary, "Methodology",
+ * layer 2): fused tasks, tiles, queue assignment, one counter per join, and
+ * per-queue orders taken from one global topological order.  Host only.
+ * AMK_ERR_UNSUPPORTED for biased projections, n_heads % n_kv_heads != 0, odd
+ * head_dim, widths the weight format cannot tile, or an unbuilt fuse_flags
+ * combination; AMK_ERR_INVALID_ARG for non-positive sizes. *out is owned by
+ * the library (amk_schedule_free). */
+amk_status amk_build_schedule(const amk_model_config* model, const amk_schedule_config* config,
+                              amk_schedule** out);
+
+/* The static safety gate (AMK summary, "Methodology", "The safety gate";
+ * rules and their order in the design doc).  AMK_OK iff the schedule is safe, else
+ * AMK_ERR_UNSAFE_SCHEDULE with *out naming the first failure.  Host only,
+ * never touches a GPU. */
+amk_status amk_validate(const amk_schedule* schedule, amk_verdict* out);
+
+/* Flat view of a schedule; the arrays stay valid until amk_schedule_free. */
+amk_status amk_schedule_view(const amk_schedule* schedule, amk_schedule_desc* out);
+
+/* Build a schedule from a caller-made description (hand-written or mutated
+ * schedules for the validator).  Copies everything; nothing is checked
+ * beyond array presence (that is amk_validate's job). */
+amk_status amk_schedule_from_desc(const amk_schedule_desc* desc, amk_schedule** out);
+
+void amk_schedule_free(amk_schedule* schedule);
+
+/* ---- weights and KV cache ------------------------------------------------ */
+
+/* Number of packed weight tensors of a model: 3 + 6 * n_layers
+ * (0 embedding, 1 final norm, 2 lm_head, then per layer attn_norm, qkv, o,
+ * mlp_norm, gate/up, down). */
+amk_status amk_packed_count(const amk_model_config* model, int32_t* out);
+
+/* Byte size of packed tensor k in device layout. */
+amk_status amk_packed_bytes(const amk_model_config* model, int32_t k, size_t* bytes);
+
+/* Pack (and for int8 / int4 models quantise) packed tensor k from canonical
+ * bf16 host tensors.  canonical[id] points to canonical tensor id in Hugging
+ * Face [out][in] order (0 embedding, 1 + 9l + {0 attn_norm, 1 wq, 2 wk, 3 wv,
+ * 4 wo, 5 mlp_norm, 6 w_gate, 7 w_up, 8 w_down}, 1 + 9L final_norm,
+ * 2 + 9L lm_head, unused when tied); only the ids packed tensor k needs are
+ * read.  dst is host memory of amk_packed_bytes bytes.  Quantisation follows
+ * the formats in the design doc (int8: s = amax/127 per row; int4: groups of 128,
+ * s = fp16((max-min)/15), z = round(-min/s)), computed in fp32. */
+amk_status amk_pack_tensor(const amk_model_config* model, int32_t k,
+                           const uint16_t* const* canonical, void* dst);
+
+/* Inverse of the layout part of amk_pack_tensor for one canonical projection
+ * inside packed tensor k (wq / wk / wv inside qkv, w_gate / w_up inside
+ * gate/up; canonical_id picks which).  Writes the canonical quantised values:
+ * bf16 bits (uint16 [rows][cols]); int8 q (int8 [rows][cols]) + fp32 scales;
+ * int4 bytes (uint8 [rows][cols/2], low nibble = even column) + fp16 scales +
+ * fp16 zeros ([rows][cols/128]).  Unused outputs may be null. */
+amk_status amk_unpack_tensor(const amk_model_config* model, int32_t k, int32_t canonical_id,
+                             const void* packed, void* q_out, void* scale_out, void* zero_out);
+
+/* KV-cache bytes: n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2. */
+amk_status amk_kv_bytes(const amk_model_config* model, size_t* bytes);
+
+/* ---- engine ---------------------------------------------------------------- */
+
+/* Bind a schedule to caller device buffers on the current HIP device.
+ * Calls amk_validate first and refuses unsafe schedules with
+ * AMK_ERR_UNSAFE_SCHEDULE before anything reaches the GPU (AMK summary,
+ * "Methodology": a schedule that fails the checks is rejected immediately).
+ * Also refuses a schedule whose queues exceed the co-resident workgroups of
+ * the device (AMK_ERR_UNSUPPORTED).  Allocates the library's sync region
+ * (counters + activation scratch) and uploads the task table. */
+amk_status amk_engine_create(const amk_schedule* schedule, const amk_device_buffers* buffers,
+                             amk_engine** out);
+
+/* One decode step: the logits of `token` at position `pos` (fp32[vocab] into
+ * buffers->logits), the KV-cache row `pos` written.  Enqueues exactly one
+ * cooperative launch on hip_stream (a hipStream_t, null = default stream) and
+ * does not synchronise.  token outside [0, vocab) or pos outside
+ * [0, max_ctx) -> AMK_ERR_OUT_OF_RANGE; pos greater than the number of
+ * positions written so far -> AMK_ERR_INVALID_ARG; pos at or below it
+ * rewinds (rows from pos on are overwritten).  One engine per stream. */
+amk_status amk_decode_step(amk_engine* engine, int32_t token, int32_t pos, void* hip_stream);
+
+/* Declare that KV-cache rows 0..n_positions-1 already hold valid state the
+ * caller wrote (a restored cache, or a prefix filled outside the library), so
+ * the next decode step may use any pos <= n_positions.  0 <= n_positions <=
+ * max_ctx, else AMK_ERR_OUT_OF_RANGE. */
+amk_status amk_engine_set_kv_length(amk_engine* engine, int32_t n_positions);
+
+/* After the caller synchronised the stream: AMK_ERR_TIMEOUT if a device-side
+ * wait gave up (the sync region is then reset and the KV rows of that step
+ * are undefined), AMK_OK otherwise. */
+amk_status amk_engine_check(amk_engine* engine);
+
+/* Per-launch spin budget in microseconds for device-side waits (default
+ * 2,000,000).  Every wait of a launch gives up once the budget is spent and
+ * the launch then drains; amk_engine_check reports it. */
+amk_status amk_engine_set_spin_budget(amk_engine* engine, int64_t microseconds);
+
+/* Host-side count of decode steps since creation (for the caller's bookkeeping). */
+amk_status amk_engine_steps(const amk_engine* engine, int64_t* out);
+
+amk_status amk_engine_destroy(amk_engine* engine);
+
+/* ---- errors ------------------------------------------------------------------ */
+
+const char* amk_status_string(amk_status status);
+const char* amk_last_error(void);  /* thread-local message of the last failure */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AMK_H */

@@ -1,0 +1,240 @@
+// C ABI entry points that run on the host only (no HIP calls): errors,
+// configuration, lowering, the safety gate, schedule views and weight packing.
+#include <algorithm>
+#include <new>
+
+#include "amk_internal.h"
+
+namespace amk {
+amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_schedule* s);
+amk_status pack_tensor(const amk_model_config& m, int32_t k, const uint16_t* const* canon, void* dst);
+amk_status unpack_tensor(const amk_model_config& m, int32_t k, int32_t canon_id, const void* packed,
+                         void* q_out, void* s_out, void* z_out);
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+amk_status fail(amk_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+}  // namespace amk
+
+using namespace amk;
+
+extern "C" {
+
+const char* amk_status_string(amk_status st) {
+  switch (st) {
+    case AMK_OK: return "AMK_OK";
+    case AMK_ERR_INVALID_ARG: return "AMK_ERR_INVALID_ARG";
+    case AMK_ERR_UNSUPPORTED: return "AMK_ERR_UNSUPPORTED";
+    case AMK_ERR_UNSAFE_SCHEDULE: return "AMK_ERR_UNSAFE_SCHEDULE";
+    case AMK_ERR_OUT_OF_RANGE: return "AMK_ERR_OUT_OF_RANGE";
+    case AMK_ERR_HIP: return "AMK_ERR_HIP";
+    case AMK_ERR_NOMEM: return "AMK_ERR_NOMEM";
+    case AMK_ERR_TIMEOUT: return "AMK_ERR_TIMEOUT";
+  }
+  return "AMK_ERR_UNKNOWN";
+}
+
+const char* amk_last_error(void) { return g_last_error.c_str(); }
+
+amk_status amk_default_schedule_config(const amk_model_config* model, int32_t device_cus,
+                                       amk_schedule_config* out) {
+  if (!model || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  if (device_cus < 1) return fail(AMK_ERR_INVALID_ARG, "device_cus must be positive");
+  amk_status st = check_model(*model);
+  if (st != AMK_OK) return st;
+  amk_schedule_config c{};
+  c.num_cus = device_cus;
+  c.wg_threads = 512;
+  c.cu_policy = 0;
+  c.pipeline_depth = 16;
+  c.fuse_flags = AMK_FUSE_DEFAULT;
+  return resolve_config(*model, c, out);
+}
+
+amk_status amk_build_schedule(const amk_model_config* model, const amk_schedule_config* config,
+                              amk_schedule** out) {
+  if (!model || !config || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  amk_status st = check_model(*model);
+  if (st != AMK_OK) return st;
+  amk_schedule_config c;
+  st = resolve_config(*model, *config, &c);
+  if (st != AMK_OK) return st;
+  amk_schedule* s = new (std::nothrow) amk_schedule();
+  if (!s) return fail(AMK_ERR_NOMEM, "out of host memory");
+  try {
+    st = lower(*model, c, s);
+  } catch (const std::bad_alloc&) {
+    st = fail(AMK_ERR_NOMEM, "out of host memory while lowering");
+  }
+  if (st != AMK_OK) {
+    delete s;
+    return st;
+  }
+  *out = s;
+  return AMK_OK;
+}
+
+amk_status amk_validate(const amk_schedule* s, amk_verdict* out) {
+  if (!s || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  try {
+    *out = validate(*s);
+  } catch (const std::bad_alloc&) {
+    return fail(AMK_ERR_NOMEM, "out of host memory while validating");
+  }
+  if (out->code != AMK_V_OK) {
+    static const char* names[] = {"OK", "REF", "THRESHOLD", "CYCLE", "QUEUE_ORDER", "UNDER_JOINED",
+                                  "RACE", "OUTPUT"};
+    return fail(AMK_ERR_UNSAFE_SCHEDULE,
+                std::string("unsafe schedule: ") + names[out->code] + " task " +
+                    std::to_string(out->task) + " counter " + std::to_string(out->counter) + " aux " +
+                    std::to_string(out->aux));
+  }
+  return AMK_OK;
+}
+
+amk_status amk_schedule_view(const amk_schedule* s, amk_schedule_desc* out) {
+  if (!s || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  const int32_t nt = (int32_t)s->tasks.size();
+  s->v_tasks.resize(nt);
+  s->v_wait_off.assign(1, 0);
+  s->v_sig_off.assign(1, 0);
+  s->v_acc_off.assign(1, 0);
+  s->v_waits.clear();
+  s->v_sigs.clear();
+  s->v_acc.clear();
+  for (int32_t i = 0; i < nt; ++i) {
+    const Task& t = s->tasks[i];
+    amk_task_desc& d = s->v_tasks[i];
+    d.type = t.type;
+    d.cu = t.cu;
+    std::copy(t.p, t.p + 8, d.p);
+    for (const Wait& w : t.waits) s->v_waits.push_back({w.ctr, w.thr});
+    for (int32_t c : t.sigs) s->v_sigs.push_back(c);
+    for (const Access& a : t.acc) s->v_acc.push_back({a.buf, a.mode, a.begin, a.end});
+    s->v_wait_off.push_back((int32_t)s->v_waits.size());
+    s->v_sig_off.push_back((int32_t)s->v_sigs.size());
+    s->v_acc_off.push_back((int32_t)s->v_acc.size());
+  }
+  s->v_queue_off.assign(1, 0);
+  s->v_queue.clear();
+  for (const auto& q : s->queues) {
+    s->v_queue.insert(s->v_queue.end(), q.begin(), q.end());
+    s->v_queue_off.push_back((int32_t)s->v_queue.size());
+  }
+  s->v_buffers.clear();
+  for (const Buffer& b : s->buffers) s->v_buffers.push_back({b.size, b.kind, 0});
+  amk_schedule_desc d{};
+  d.model = s->model;
+  d.config = s->config;
+  d.n_tasks = nt;
+  d.n_counters = s->n_counters;
+  d.n_buffers = (int32_t)s->buffers.size();
+  d.n_cus = (int32_t)s->queues.size();
+  d.tasks = s->v_tasks.data();
+  d.wait_off = s->v_wait_off.data();
+  d.waits = s->v_waits.data();
+  d.sig_off = s->v_sig_off.data();
+  d.sigs = s->v_sigs.data();
+  d.acc_off = s->v_acc_off.data();
+  d.accesses = s->v_acc.data();
+  d.queue_off = s->v_queue_off.data();
+  d.queue = s->v_queue.data();
+  d.buffers = s->v_buffers.data();
+  *out = d;
+  return AMK_OK;
+}
+
+amk_status amk_schedule_from_desc(const amk_schedule_desc* d, amk_schedule** out) {
+  if (!d || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (d->n_tasks < 0 || d->n_counters < 0 || d->n_buffers < 0 || d->n_cus < 0)
+    return fail(AMK_ERR_INVALID_ARG, "negative count");
+  if (!d->wait_off || !d->sig_off || !d->acc_off || !d->queue_off ||
+      (d->n_tasks && !d->tasks) || (d->n_buffers && !d->buffers))
+    return fail(AMK_ERR_INVALID_ARG, "missing array");
+  auto csr_ok = [](const int32_t* off, int32_t n, const void* arr) {
+    if (off[0] != 0) return false;
+    for (int32_t i = 0; i < n; ++i)
+      if (off[i + 1] < off[i]) return false;
+    return off[n] == 0 || arr != nullptr;
+  };
+  if (!csr_ok(d->wait_off, d->n_tasks, d->waits) || !csr_ok(d->sig_off, d->n_tasks, d->sigs) ||
+      !csr_ok(d->acc_off, d->n_tasks, d->accesses) || !csr_ok(d->queue_off, d->n_cus, d->queue))
+    return fail(AMK_ERR_INVALID_ARG, "malformed CSR offsets");
+  amk_schedule* s = new (std::nothrow) amk_schedule();
+  if (!s) return fail(AMK_ERR_NOMEM, "out of host memory");
+  s->model = d->model;
+  s->config = d->config;
+  s->n_counters = d->n_counters;
+  s->tasks.resize(d->n_tasks);
+  for (int32_t i = 0; i < d->n_tasks; ++i) {
+    Task& t = s->tasks[i];
+    t.type = d->tasks[i].type;
+    t.cu = d->tasks[i].cu;
+    std::copy(d->tasks[i].p, d->tasks[i].p + 8, t.p);
+    for (int32_t k = d->wait_off[i]; k < d->wait_off[i + 1]; ++k)
+      t.waits.push_back({d->waits[k].counter, d->waits[k].threshold});
+    for (int32_t k = d->sig_off[i]; k < d->sig_off[i + 1]; ++k) t.sigs.push_back(d->sigs[k]);
+    for (int32_t k = d->acc_off[i]; k < d->acc_off[i + 1]; ++k)
+      t.acc.push_back({d->accesses[k].buffer, d->accesses[k].mode, d->accesses[k].begin, d->accesses[k].end});
+  }
+  s->queues.resize(d->n_cus);
+  for (int32_t c = 0; c < d->n_cus; ++c)
+    s->queues[c].assign(d->queue + d->queue_off[c], d->queue + d->queue_off[c + 1]);
+  for (int32_t b = 0; b < d->n_buffers; ++b) s->buffers.push_back({d->buffers[b].size, d->buffers[b].kind});
+  *out = s;
+  return AMK_OK;
+}
+
+void amk_schedule_free(amk_schedule* s) { delete s; }
+
+amk_status amk_packed_count(const amk_model_config* m, int32_t* out) {
+  if (!m || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_status st = check_model(*m);
+  if (st != AMK_OK) return st;
+  *out = 3 + 6 * m->n_layers;
+  return AMK_OK;
+}
+
+amk_status amk_packed_bytes(const amk_model_config* m, int32_t k, size_t* bytes) {
+  if (!m || !bytes) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_status st = check_model(*m);
+  if (st != AMK_OK) return st;
+  if (k < 0 || k >= 3 + 6 * m->n_layers) return fail(AMK_ERR_OUT_OF_RANGE, "packed tensor id out of range");
+  *bytes = (size_t)packed_layout(*m, k).total_bytes();
+  return AMK_OK;
+}
+
+amk_status amk_pack_tensor(const amk_model_config* m, int32_t k, const uint16_t* const* canonical,
+                           void* dst) {
+  if (!m || !canonical || !dst) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_status st = check_model(*m);
+  if (st != AMK_OK) return st;
+  if (k < 0 || k >= 3 + 6 * m->n_layers) return fail(AMK_ERR_OUT_OF_RANGE, "packed tensor id out of range");
+  return pack_tensor(*m, k, canonical, dst);
+}
+
+amk_status amk_unpack_tensor(const amk_model_config* m, int32_t k, int32_t canonical_id,
+                             const void* packed, void* q_out, void* scale_out, void* zero_out) {
+  if (!m || !packed) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_status st = check_model(*m);
+  if (st != AMK_OK) return st;
+  if (k < 0 || k >= 3 + 6 * m->n_layers) return fail(AMK_ERR_OUT_OF_RANGE, "packed tensor id out of range");
+  return unpack_tensor(*m, k, canonical_id, packed, q_out, scale_out, zero_out);
+}
+
+amk_status amk_kv_bytes(const amk_model_config* m, size_t* bytes) {
+  if (!m || !bytes) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_status st = check_model(*m);
+  if (st != AMK_OK) return st;
+  *bytes = (size_t)m->n_layers * 2 * m->n_kv_heads * m->max_ctx * m->head_dim * 2;
+  return AMK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Lowering of a Llama-style decoder to the typed Schedule DAG (the layer-2
+// "Scheduler" of the AutoMegaKernel summary, section "Methodology": import the
+// model, lower it to a task DAG synchronised by monotonic counters, under a
+// ScheduleConfig of tiling, fusion, SM assignment and pipelining depth).
+//
+// Per layer l the fused task phases are
+//   QKV    RMSNorm prologue, q/k/v rows, RoPE, K/V row written at pos
+//   ATTN   one split of the positions of one kv head, for its query group
+//   MERGE  log-sum-exp merge of the splits of one query head
+//   OPROJ  o-projection rows + residual
+//   GATEUP RMSNorm prologue, gate/up rows, silu(gate)*up
+//   DOWN   down-projection rows + residual
+// and one LMHEAD phase (final RMSNorm prologue + vocabulary rows) at the end.
+// Each join is one counter whose waiters wait for all its producers:
+//   QKV(l) <- DOWN(l-1);  ATTN(l) <- QKV(l);  MERGE(l,h) <- ATTN(l, group of h);
+//   OPROJ(l) <- MERGE(l);  GATEUP(l) <- OPROJ(l);  DOWN(l) <- GATEUP(l);
+//   LMHEAD <- DOWN(L-1).
+// Task ids follow one global topological order (phase by phase) and every
+// queue lists its tasks in that order.
+#include <algorithm>
+
+#include "amk_internal.h"
+
+namespace amk {
+
+namespace {
+
+struct Builder {
+  amk_schedule* s;
+  const amk_model_config& m;
+  const amk_schedule_config& c;
+
+  int32_t counter() { return s->n_counters++; }
+
+  int32_t cu_of(int64_t i, int64_t T) const {
+    if (c.cu_policy == 1) return (int32_t)(i % c.num_cus);
+    return (int32_t)((i * c.num_cus) / T);
+  }
+
+  int32_t add(int32_t type, int32_t cu, std::initializer_list<int32_t> params,
+              std::initializer_list<Wait> waits, std::initializer_list<int32_t> sigs) {
+    Task t;
+    t.type = type;
+    t.cu = cu;
+    int k = 0;
+    for (int32_t v : params) t.p[k++] = v;
+    t.waits.assign(waits);
+    t.sigs.assign(sigs);
+    derive_accesses(m, t, &t.acc);
+    sort_accesses(&t.acc);
+    s->tasks.push_back(std::move(t));
+    return (int32_t)s->tasks.size() - 1;
+  }
+};
+
+// bounds of piece i when n items are split into T nearly equal pieces
+inline int64_t split_at(int64_t n, int64_t T, int64_t i) { return (n * i) / T; }
+
+}  // namespace
+
+amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_schedule* s) {
+  Builder b{s, m, c};
+  s->model = m;
+  s->config = c;
+  s->tasks.clear();
+  s->n_counters = 0;
+  const int32_t L = m.n_layers, nq = m.n_heads, nkv = m.n_kv_heads, grp = nq / nkv;
+  const int64_t U = (int64_t)(nq + 2 * nkv) * (m.head_dim / 2);
+  const int32_t S = c.attn_splits;
+  const uint32_t Pq = c.tiles_qkv, Pattn = S, Pm = nq, Po = c.tiles_o, Pg = c.tiles_gateup,
+                 Pd = c.tiles_down;
+  int32_t prev_down = -1;
+  for (int32_t l = 0; l < L; ++l) {
+    const int32_t c_qkv = b.counter();
+    std::vector<int32_t> c_attn(nkv);
+    for (int32_t g = 0; g < nkv; ++g) c_attn[g] = b.counter();
+    const int32_t c_merge = b.counter(), c_o = b.counter(), c_gu = b.counter(), c_down = b.counter();
+    for (int32_t i = 0; i < c.tiles_qkv; ++i) {
+      const int32_t u0 = (int32_t)split_at(U, c.tiles_qkv, i), u1 = (int32_t)split_at(U, c.tiles_qkv, i + 1);
+      if (l == 0) b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {}, {c_qkv});
+      else b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {{prev_down, Pd}}, {c_qkv});
+    }
+    const int64_t n_attn = (int64_t)nkv * S;
+    for (int32_t g = 0; g < nkv; ++g)
+      for (int32_t sp = 0; sp < S; ++sp)
+        b.add(AMK_TASK_ATTN, b.cu_of((int64_t)g * S + sp, n_attn), {l, g, sp, S}, {{c_qkv, Pq}},
+              {c_attn[g]});
+    for (int32_t h = 0; h < nq; ++h)
+      b.add(AMK_TASK_MERGE, b.cu_of(h, nq), {l, h, S}, {{c_attn[h / grp], Pattn}}, {c_merge});
+    for (int32_t i = 0; i < c.tiles_o; ++i)
+      b.add(AMK_TASK_OPROJ, b.cu_of(i, c.tiles_o),
+            {l, (int32_t)split_at(m.hidden, c.tiles_o, i), (int32_t)split_at(m.hidden, c.tiles_o, i + 1)},
+            {{c_merge, Pm}}, {c_o});
+    for (int32_t i = 0; i < c.tiles_gateup; ++i)
+      b.add(AMK_TASK_GATEUP, b.cu_of(i, c.tiles_gateup),
+            {l, (int32_t)split_at(m.ffn, c.tiles_gateup, i), (int32_t)split_at(m.ffn, c.tiles_gateup, i + 1)},
+            {{c_o, Po}}, {c_gu});
+    for (int32_t i = 0; i < c.tiles_down; ++i)
+      b.add(AMK_TASK_DOWN, b.cu_of(i, c.tiles_down),
+            {l, (int32_t)split_at(m.hidden, c.tiles_down, i), (int32_t)split_at(m.hidden, c.tiles_down, i + 1)},
+            {{c_gu, Pg}}, {c_down});
+    prev_down = c_down;
+  }
+  const int32_t c_lm = b.counter();
+  for (int32_t i = 0; i < c.tiles_lm; ++i)
+    b.add(AMK_TASK_LMHEAD, b.cu_of(i, c.tiles_lm),
+          {(int32_t)split_at(m.vocab, c.tiles_lm, i), (int32_t)split_at(m.vocab, c.tiles_lm, i + 1)},
+          {{prev_down, Pd}}, {c_lm});
+  s->queues.assign(c.num_cus, {});
+  for (int32_t t = 0; t < (int32_t)s->tasks.size(); ++t) s->queues[s->tasks[t].cu].push_back(t);
+  s->buffers = buffer_table(m, S);
+  return AMK_OK;
+}
+
+}  // namespace amk

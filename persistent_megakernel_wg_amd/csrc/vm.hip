@@ -1,0 +1,1252 @@
+// The persistent decode megakernel for gfx950 (CDNA4) and its engine.
+//
+// One cooperative launch per decode step; workgroup b (512 threads, 8
+// wave64s) walks queue b of the schedule: for every task it waits until its
+// counters reach epoch*P + t, runs the task's micro-kernel, and signals its
+// counters (AutoMegaKernel summary, section "Methodology", layer 0: one
+// cooperative block per multiprocessor with a local queue over a global
+// topological order, wait -> dispatch -> signal on monotonic counters, no
+// locks).  Micro-kernels (layer 1 of the same section): fused RMSNorm
+// prologue + GEMV for the projections, RoPE + KV append, split decode
+// attention with a log-sum-exp merge, SwiGLU, residual epilogues, LM head.
+//
+// GEMV design (HBM-bound, batch 1): each wave owns whole output rows (or a
+// RoPE / gate-up pair of rows), streams them with 16-byte buffer loads (64
+// lanes read 1 KB contiguous per instruction), keeps `DEPTH` loads per lane
+// in flight in a register ring, and multiplies against the activation vector
+// staged in LDS.  The first DEPTH loads of a task are issued BEFORE its wait,
+// so weight streaming continues while the workgroup waits on a counter (the
+// "deeper pipelining" the AMK summary names as the remedy for per-tile sync
+// cost on high-bandwidth GPUs, section "Experimental results", training-class
+// GPUs).  Buffer loads whose offset is past the task's rows return zero
+// without touching memory, so ring tails cost no bandwidth.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "amk_internal.h"
+
+namespace amk {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr uint32_t kOob = 0x80000000u;       // offset past every descriptor range
+
+struct VmParams {
+  const DevTask* tasks;
+  const int32_t* queue_off;
+  const int32_t* queue;
+  const uint8_t* const* wptr;  // packed tensors [3 + 6L]
+  uint16_t* kv;                // [L][2][nkv][mc][hd] bf16
+  float* logits;
+  float* x;     // [L][2][H]
+  float* q;     // [L][nq*hd]
+  float* part;  // [L][nq][S][hd+2]
+  float* o;     // [L][nq*hd]
+  float* a;     // [L][F]
+  uint32_t* ctr;
+  int32_t* err;
+  const float2* rope;  // [mc][hd/2] (cos, sin)
+  uint64_t spin_ticks;
+  int32_t token, pos;
+  uint32_t epoch;
+  int32_t L, H, nq, nkv, hd, F, V, mc, S, wfmt, act_bf16;
+  float eps;
+  // LDS carve-up (float offsets into dynamic shared memory)
+  int32_t lds_x, lds_res, lds_att;
+  int32_t att_maxlen;
+};
+
+// ------------------------------------------------------------- helpers --
+
+// threadIdx.x through an opaque move: values derived from it cannot be
+// hoisted out of one task into the queue loop, where the per-lane addresses
+// of every inlined micro-kernel would otherwise stay live at once.
+__device__ __forceinline__ int opaque_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to the nearest bf16 (ties to even); values are finite here
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(bf16_bits(f) << 16); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// sum over the workgroup; `red` holds kWaves floats of LDS
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((opaque_tid() & 63) == 0) red[opaque_tid() >> 6] = v;
+  __syncthreads();
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// relaxed agent-scope load: a vector load that no cache level keeps stale
+// across the acquire done by the waiting thread
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufFlags);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// ------------------------------------------------------- wait / signal --
+
+// Thread 0 spins until every wait of the task holds, then performs the
+// agent-scope acquire; the workgroup barrier passes the result to all
+// threads.  Returns false when the spin budget ran out or another
+// workgroup already reported an error (the launch then drains).
+__device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int* flag) {
+  if (opaque_tid() == 0) {
+    int ok = 1;
+    for (int k = 0; k < t.nwait && ok; ++k) {
+      const uint32_t target = P.epoch * t.wprod[k] + t.wthr[k];
+      uint32_t* c = P.ctr + (size_t)t.wctr[k] * kCounterStride;
+      const uint64_t start = wall_clock64();
+      uint32_t polls = 0;
+      while ((int32_t)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++polls & 63u) == 0u) {
+          if (__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+              wall_clock64() - start > P.spin_ticks) {
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    if (!ok) __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// All threads' stores are ordered before the barrier; thread 0 then
+// releases at agent scope and bumps each counter once.
+__device__ __forceinline__ void vm_signal(const VmParams& P, const DevTask& t) {
+  __syncthreads();
+  if (opaque_tid() == 0 && t.nsig > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int k = 0; k < t.nsig; ++k)
+      __hip_atomic_fetch_add(P.ctr + (size_t)t.sctr[k] * kCounterStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------- staging --
+// The activation vector of a GEMV is staged in LDS permuted so that lane l
+// of wave-load j reads its 8 values as two conflict-free float4 reads:
+// element e (chunk c = e/8, k = e%8, j = c/64, lane = c%64) lives at
+// ((j*2 + k/4)*64 + lane)*4 + k%4.  Padding up to whole wave-loads is zero.
+__device__ __forceinline__ int xperm(int e) {
+  const int c = e >> 3, k = e & 7;
+  return (((c >> 6) * 2 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
+}
+
+// x (fp32 or bf16 source) -> optional RMSNorm with bf16 gain -> optional bf16
+// rounding -> LDS.  n is a multiple of 8.
+template <bool SRC_BF16, bool NORM>
+__device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
+                        float* xs, float* red) {
+  const int n4 = n >> 2;
+  float ss = 0.0f;
+  for (int i = opaque_tid(); i < n4; i += kThreads) {
+    float4 v;
+    if (SRC_BF16) {
+      const uint2 b = reinterpret_cast<const uint2*>(src)[i];
+      v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+    } else {
+      v = reinterpret_cast<const float4*>(src)[i];
+    }
+    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    if (!NORM && act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+    *reinterpret_cast<float4*>(xs + xperm(i * 4)) = v;
+  }
+  // zero padding of the last wave-load
+  const int padded = ((n + 511) >> 9) << 9;
+  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
+    *reinterpret_cast<float4*>(xs + xperm(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (NORM) {
+    const float tot = block_sum(ss, red);  // contains barriers
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    for (int i = opaque_tid(); i < n4; i += kThreads) {
+      float4* p = reinterpret_cast<float4*>(xs + xperm(i * 4));
+      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
+      float4 v = *p;
+      v.x = v.x * inv * bf16_lo(g.x);
+      v.y = v.y * inv * bf16_hi(g.x);
+      v.z = v.z * inv * bf16_lo(g.y);
+      v.w = v.w * inv * bf16_hi(g.y);
+      if (act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+      *p = v;
+    }
+  }
+  __syncthreads();
+}
+
+// --------------------------------------------------------------- GEMV ---
+// bf16 rows.  `base` = first packed row of the task, `row_bytes` = K*2,
+// `nunits` units of RPU consecutive rows.  Wave w owns units w, w+8, ...
+// After the prologue issues the first DS steps (RPU loads each), `stage()`
+// runs the wait and the staging; results land in res[unit*RPU + r].
+template <int DS, int RPU, typename StageFn>
+__device__ __forceinline__ void gemv_bf16(const uint8_t* base, uint32_t row_bytes, int nunits, int K,
+                                          const float* xs, float* res, StageFn&& stage) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int nchunk = K >> 3;             // 16-byte chunks per row
+  const int J = (nchunk + 63) >> 6;      // wave-loads per row
+  const int jl = (nchunk - lane + 63) >> 6;  // wave-loads in which this lane has data
+  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base, (uint32_t)nunits * RPU * row_bytes);
+  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
+
+  int ik = 0, ij = 0;
+  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
+  u32x4 buf[DS][RPU];
+  auto issue = [&](u32x4 (&b)[RPU]) {
+    const bool valid = ik < nk && ij < jl;
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
+    ioff += 1024u;
+    if (++ij == J) {
+      ij = 0;
+      ++ik;
+      ioff += unit_step;
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    issue(buf[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage();
+  const int total = nk * J;
+  const int iters = (total + DS - 1) / DS;
+  float acc[RPU];
+#pragma unroll
+  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
+  int cj = 0, ck = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const float4 xa = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 0) * 64 + lane) * 4);
+      const float4 xb = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 1) * 64 + lane) * 4);
+#pragma unroll
+      for (int r = 0; r < RPU; ++r) {
+        const u32x4 w = buf[s][r];
+        float t = acc[r];
+        t = fmaf(bf16_lo(w.x), xa.x, t);
+        t = fmaf(bf16_hi(w.x), xa.y, t);
+        t = fmaf(bf16_lo(w.y), xa.z, t);
+        t = fmaf(bf16_hi(w.y), xa.w, t);
+        t = fmaf(bf16_lo(w.z), xb.x, t);
+        t = fmaf(bf16_hi(w.z), xb.y, t);
+        t = fmaf(bf16_lo(w.w), xb.z, t);
+        t = fmaf(bf16_hi(w.w), xb.w, t);
+        acc[r] = t;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[s]);
+      if (++cj == J) {
+        cj = 0;
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const float v = wave_sum(acc[r]);
+          if (lane == 0 && ck < nk) res[(wave + ck * kWaves) * RPU + r] = v;
+          acc[r] = 0.0f;
+        }
+        ++ck;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// int8 rows stored as q + 128 with one fp32 scale per row after the data:
+// row = s_r * (sum_k u_k x_k - 128 * sum_k x_k).  Chunks are 16 values; the
+// staged x uses 16-value chunks: element e (c = e/16, k = e%16, j = c/64) at
+// ((j*4 + k/4)*64 + c%64)*4 + k%4.
+__device__ __forceinline__ int xperm16(int e) {
+  const int c = e >> 4, k = e & 15;
+  return (((c >> 6) * 4 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
+}
+
+template <bool SRC_BF16, bool NORM>
+__device__ __forceinline__ void stage_x16(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
+                          float* xs, float* red, float* xsum) {
+  const int n4 = n >> 2;
+  float ss = 0.0f;
+  for (int i = opaque_tid(); i < n4; i += kThreads) {
+    float4 v;
+    if (SRC_BF16) {
+      const uint2 b = reinterpret_cast<const uint2*>(src)[i];
+      v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+    } else {
+      v = reinterpret_cast<const float4*>(src)[i];
+    }
+    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    *reinterpret_cast<float4*>(xs + xperm16(i * 4)) = v;
+  }
+  const int padded = ((n + 1023) >> 10) << 10;
+  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
+    *reinterpret_cast<float4*>(xs + xperm16(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  float inv = 1.0f;
+  if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
+  else __syncthreads();
+  float sx = 0.0f;
+  for (int i = opaque_tid(); i < n4; i += kThreads) {
+    float4* p = reinterpret_cast<float4*>(xs + xperm16(i * 4));
+    float4 v = *p;
+    if (NORM) {
+      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
+      v.x = v.x * inv * bf16_lo(g.x);
+      v.y = v.y * inv * bf16_hi(g.x);
+      v.z = v.z * inv * bf16_lo(g.y);
+      v.w = v.w * inv * bf16_hi(g.y);
+    }
+    if (act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+    *p = v;
+    sx += v.x + v.y + v.z + v.w;
+  }
+  const float tot = block_sum(sx, red);
+  if (opaque_tid() == 0) *xsum = tot;
+  __syncthreads();
+}
+
+template <int DS, int RPU, typename StageFn>
+__device__ __forceinline__ void gemv_int8(const uint8_t* data, const float* scales, uint32_t row_bytes,
+                                          int nunits, int K, const float* xs, const float* xsum,
+                                          float* res, StageFn&& stage) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int nchunk = K >> 4;
+  const int J = (nchunk + 63) >> 6;
+  const int jl = (nchunk - lane + 63) >> 6;
+  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
+  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
+  int ik = 0, ij = 0;
+  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
+  u32x4 buf[DS][RPU];
+  auto issue = [&](u32x4 (&b)[RPU]) {
+    const bool valid = ik < nk && ij < jl;
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
+    ioff += 1024u;
+    if (++ij == J) {
+      ij = 0;
+      ++ik;
+      ioff += unit_step;
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    issue(buf[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage();
+  const float sum_x = *xsum;
+  const int total = nk * J;
+  const int iters = (total + DS - 1) / DS;
+  float acc[RPU];
+#pragma unroll
+  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
+  int cj = 0, ck = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      float4 xv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[q] = *reinterpret_cast<const float4*>(xs + ((cj * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+      for (int r = 0; r < RPU; ++r) {
+        const u32x4 w = buf[s][r];
+        float t = acc[r];
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          t = fmaf((float)((wd[q] >> 0) & 0xFFu), xv[q].x, t);
+          t = fmaf((float)((wd[q] >> 8) & 0xFFu), xv[q].y, t);
+          t = fmaf((float)((wd[q] >> 16) & 0xFFu), xv[q].z, t);
+          t = fmaf((float)((wd[q] >> 24) & 0xFFu), xv[q].w, t);
+        }
+        acc[r] = t;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[s]);
+      if (++cj == J) {
+        cj = 0;
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const float v = wave_sum(acc[r]);
+          if (lane == 0 && ck < nk) {
+            const int row = (wave + ck * kWaves) * RPU + r;
+            res[row] = scales[row] * (v - 128.0f * sum_x);
+          }
+          acc[r] = 0.0f;
+        }
+        ++ck;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// int4 rows: per row K/2 bytes (nibbles permuted so that (w >> 4j) &
+// 0x000F000F gives columns 2j, 2j+1 of an 8-column word), then per row K/128
+// {fp16 scale, fp16 zero}.  A 16-byte chunk is 32 columns = a quarter group.
+// Staged x: 32-value chunks, element e (c = e/32, k = e%32, j = c/64) at
+// ((j*8 + k/4)*64 + c%64)*4 + k%4, plus per-chunk sums of x.
+__device__ __forceinline__ int xperm32(int e) {
+  const int c = e >> 5, k = e & 31;
+  return (((c >> 6) * 8 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
+}
+
+template <bool SRC_BF16, bool NORM>
+__device__ __forceinline__ void stage_x32(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
+                          float* xs, float* red, float* csum) {
+  const int n4 = n >> 2;
+  float ss = 0.0f;
+  for (int i = opaque_tid(); i < n4; i += kThreads) {
+    float4 v;
+    if (SRC_BF16) {
+      const uint2 b = reinterpret_cast<const uint2*>(src)[i];
+      v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+    } else {
+      v = reinterpret_cast<const float4*>(src)[i];
+    }
+    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    *reinterpret_cast<float4*>(xs + xperm32(i * 4)) = v;
+  }
+  const int padded = ((n + 2047) >> 11) << 11;
+  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
+    *reinterpret_cast<float4*>(xs + xperm32(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  float inv = 1.0f;
+  if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
+  else __syncthreads();
+  for (int i = opaque_tid(); i < n4; i += kThreads) {
+    float4* p = reinterpret_cast<float4*>(xs + xperm32(i * 4));
+    float4 v = *p;
+    if (NORM) {
+      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
+      v.x = v.x * inv * bf16_lo(g.x);
+      v.y = v.y * inv * bf16_hi(g.x);
+      v.z = v.z * inv * bf16_lo(g.y);
+      v.w = v.w * inv * bf16_hi(g.y);
+    }
+    if (act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+    *p = v;
+  }
+  __syncthreads();
+  // per-chunk sums of x (32 values each)
+  const int nch = padded >> 5;
+  for (int c = opaque_tid(); c < nch; c += kThreads) {
+    float s = 0.0f;
+    for (int k = 0; k < 32; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xs + xperm32(c * 32 + k));
+      s += v.x + v.y + v.z + v.w;
+    }
+    csum[c] = s;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float f16_to_f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+template <int DS, int RPU, typename StageFn>
+__device__ __forceinline__ void gemv_int4(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
+                                          uint32_t meta_row_bytes, int nunits, int K, const float* xs,
+                                          const float* csum, float* res, StageFn&& stage) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int nchunk = K >> 5;
+  const int J = (nchunk + 63) >> 6;
+  const int jl = (nchunk - lane + 63) >> 6;
+  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
+  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, (uint32_t)nunits * RPU * meta_row_bytes);
+  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
+  const uint32_t unit_mstep = (uint32_t)kWaves * RPU * meta_row_bytes - (uint32_t)J * 64u;
+  int ik = 0, ij = 0;
+  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
+  // group of this lane's chunk: (j*64 + lane)/4 -> meta offset 4*group
+  uint32_t moff = (uint32_t)wave * RPU * meta_row_bytes + (uint32_t)(lane >> 2) * 4u;
+  u32x4 buf[DS][RPU];
+  uint32_t mbuf[DS][RPU];
+  auto issue = [&](u32x4 (&b)[RPU], uint32_t (&m)[RPU]) {
+    const bool valid = ik < nk && ij < jl;
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) {
+      b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
+      m[r] = __builtin_amdgcn_raw_buffer_load_b32(rm, valid ? moff + (uint32_t)r * meta_row_bytes : kOob, 0, 0);
+    }
+    ioff += 1024u;
+    moff += 64u;
+    if (++ij == J) {
+      ij = 0;
+      ++ik;
+      ioff += unit_step;
+      moff += unit_mstep;
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    issue(buf[s], mbuf[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage();
+  const int total = nk * J;
+  const int iters = (total + DS - 1) / DS;
+  float acc[RPU];
+#pragma unroll
+  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
+  int cj = 0, ck = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      float4 xv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xv[q] = *reinterpret_cast<const float4*>(xs + ((cj * 8 + q) * 64 + lane) * 4);
+      const float cs = csum[cj * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < RPU; ++r) {
+        const u32x4 w = buf[s][r];
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        float d = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // word q holds columns 8q..8q+7 of the chunk; nibble j -> column 2j,
+          // nibble j+4 -> column 2j+1
+#pragma unroll
+          for (int jn = 0; jn < 4; ++jn) {
+            const float lo = (float)((wd[q] >> (4 * jn)) & 0xFu);
+            const float hi = (float)((wd[q] >> (4 * jn + 16)) & 0xFu);
+            const float4 xx = xv[q * 2 + (jn >> 1)];
+            const float x0 = (jn & 1) ? xx.z : xx.x;
+            const float x1 = (jn & 1) ? xx.w : xx.y;
+            d = fmaf(lo, x0, d);
+            d = fmaf(hi, x1, d);
+          }
+        }
+        const uint32_t m = mbuf[s][r];
+        acc[r] = fmaf(f16_to_f(m & 0xFFFFu), d - f16_to_f(m >> 16) * cs, acc[r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[s], mbuf[s]);
+      if (++cj == J) {
+        cj = 0;
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const float v = wave_sum(acc[r]);
+          if (lane == 0 && ck < nk) res[(wave + ck * kWaves) * RPU + r] = v;
+          acc[r] = 0.0f;
+        }
+        ++ck;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Runs the projection rows [row0, row0 + nunits*RPU) of packed tensor `ptr`
+// in the model's weight format.  stage_src/norm describe the input vector.
+template <int DEPTH, int RPU, bool SRC_BF16, bool NORM>
+__device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, float* smem, const uint8_t* ptr,
+                        int64_t rows_total, int K, int row0, int nunits, const void* src,
+                        const uint16_t* gain) {
+  float* red = smem;               // kWaves floats
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  float* scal = smem + kWaves + 1;  // one float (int8 sum of x)
+  float* xs = smem + P.lds_x;
+  float* res = smem + P.lds_res;
+  bool ok = true;
+  constexpr int DS = DEPTH / RPU;
+  if (P.wfmt == AMK_W_BF16) {
+    const uint32_t rb = (uint32_t)K * 2u;
+    gemv_bf16<DS, RPU>(ptr + (int64_t)row0 * rb, rb, nunits, K, xs, res, [&] {
+      ok = vm_wait(P, t, flag);
+      if (ok) stage_x<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red);
+    });
+  } else if (P.wfmt == AMK_W_INT8_ROW) {
+    const uint32_t rb = (uint32_t)K;
+    const float* scales = reinterpret_cast<const float*>(ptr + rows_total * (int64_t)K) + row0;
+    gemv_int8<DS, RPU>(ptr + (int64_t)row0 * rb, scales, rb, nunits, K, xs, scal, res, [&] {
+      ok = vm_wait(P, t, flag);
+      if (ok) stage_x16<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, scal);
+    });
+  } else {
+    const uint32_t rb = (uint32_t)K / 2u, mb = (uint32_t)(K / 128) * 4u;
+    const uint8_t* meta = ptr + rows_total * (int64_t)rb + (int64_t)row0 * mb;
+    float* csum = xs + (((K + 2047) >> 11) << 11);
+    gemv_int4<DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, res, [&] {
+      ok = vm_wait(P, t, flag);
+      if (ok) stage_x32<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, csum);
+    });
+  }
+  return ok;
+}
+
+// ---------------------------------------------------------------- tasks --
+
+template <int DEPTH>
+__device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], u0 = t.p[1], u1 = t.p[2];
+  const int H = P.H, hd = P.hd, half = hd >> 1, nq = P.nq, nkv = P.nkv;
+  const uint8_t* w = P.wptr[3 + 6 * l + LB_QKV];
+  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_ATTN_NORM]);
+  const int64_t rows = (int64_t)(nq + 2 * nkv) * hd;
+  bool ok;
+  if (l == 0) {
+    const void* src = P.wptr[0] + (int64_t)P.token * H * 2;
+    ok = project<DEPTH, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+  } else {
+    const void* src = P.x + ((int64_t)(l - 1) * 2 + 1) * H;
+    ok = project<DEPTH, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+  }
+  if (!ok) return false;
+  const float* res = smem + P.lds_res;
+  for (int k = opaque_tid(); k < u1 - u0; k += kThreads) {
+    const int u = u0 + k, hs = u / half, i = u - hs * half;
+    float a = res[2 * k], b = res[2 * k + 1];
+    if (hs < nq + nkv) {
+      const float2 cs = P.rope[(int64_t)P.pos * half + i];
+      const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
+      a = ra;
+      b = rb;
+    }
+    if (hs < nq) {
+      float* qd = P.q + (int64_t)l * nq * hd + (int64_t)hs * hd;
+      qd[i] = a;
+      qd[i + half] = b;
+    } else {
+      const int kvsel = hs < nq + nkv ? 0 : 1, g = hs - nq - kvsel * nkv;
+      uint16_t* row = P.kv + ((((int64_t)l * 2 + kvsel) * nkv + g) * P.mc + P.pos) * hd;
+      row[i] = (uint16_t)bf16_bits(a);
+      row[i + half] = (uint16_t)bf16_bits(b);
+    }
+  }
+  vm_signal(P, t);
+  return true;
+}
+
+template <int DEPTH>
+__device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
+  const int H = P.H, qd = P.nq * P.hd;
+  const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
+  const float* src = P.o + (int64_t)l * qd;
+  if (!project<DEPTH, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)) return false;
+  const float* res = smem + P.lds_res;
+  float* dst = P.x + (int64_t)l * 2 * H;
+  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) {
+    const int r = r0 + k;
+    float resid;
+    if (l == 0) resid = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
+    else resid = P.x[((int64_t)(l - 1) * 2 + 1) * H + r];
+    dst[r] = resid + res[k];
+  }
+  vm_signal(P, t);
+  return true;
+}
+
+template <int DEPTH>
+__device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], j0 = t.p[1], j1 = t.p[2];
+  const int H = P.H, F = P.F;
+  const uint8_t* w = P.wptr[3 + 6 * l + LB_GATEUP];
+  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_MLP_NORM]);
+  const float* src = P.x + (int64_t)l * 2 * H;
+  if (!project<DEPTH, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, gain))
+    return false;
+  const float* res = smem + P.lds_res;
+  float* dst = P.a + (int64_t)l * F;
+  for (int k = opaque_tid(); k < j1 - j0; k += kThreads) {
+    const float g = res[2 * k], u = res[2 * k + 1];
+    dst[j0 + k] = g / (1.0f + expf(-g)) * u;
+  }
+  vm_signal(P, t);
+  return true;
+}
+
+template <int DEPTH>
+__device__ __forceinline__ bool task_down(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
+  const int H = P.H, F = P.F;
+  const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
+  const float* src = P.a + (int64_t)l * F;
+  if (!project<DEPTH, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)) return false;
+  const float* res = smem + P.lds_res;
+  const float* mid = P.x + (int64_t)l * 2 * H;
+  float* dst = P.x + ((int64_t)l * 2 + 1) * H;
+  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) dst[r0 + k] = mid[r0 + k] + res[k];
+  vm_signal(P, t);
+  return true;
+}
+
+template <int DEPTH>
+__device__ __forceinline__ bool task_lmhead(const VmParams& P, const DevTask& t, float* smem) {
+  const int r0 = t.p[0], r1 = t.p[1];
+  const int H = P.H;
+  const uint8_t* w = P.wptr[2];
+  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
+  const float* src = P.x + ((int64_t)(P.L - 1) * 2 + 1) * H;
+  if (!project<DEPTH, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)) return false;
+  const float* res = smem + P.lds_res;
+  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
+  vm_signal(P, t);
+  return true;
+}
+
+// One split of the positions of kv head g for its GRP query heads.
+// Partials: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
+template <int GRP>
+__device__ __forceinline__ void attn_block(const VmParams& P, int l, int g, int h0, int s, int S, int p0, int len,
+                           float* smem) {
+  const int hd = P.hd, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int LP = hd >> 3, PPW = 64 / LP, sub = lane / LP, li = lane - sub * LP;
+  float* red = smem;
+  float* qs = smem + P.lds_att;                 // GRP*hd
+  float* sc = qs + GRP * hd;                    // GRP*maxlen
+  float* stats = sc + GRP * P.att_maxlen;       // 2*GRP
+  float* ored = stats + 2 * GRP;                // kWaves*GRP*hd
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int i = opaque_tid(); i < GRP * hd; i += kThreads)
+    qs[i] = P.q[(int64_t)l * P.nq * hd + (int64_t)h0 * hd + i];
+  __syncthreads();
+  const uint16_t* Kb = P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd;
+  const uint16_t* Vb = P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd;
+  // pass 1: scores
+  for (int jb = wave * PPW; jb < len; jb += kWaves * PPW) {
+    const int j = jb + sub;
+    const bool ok = j < len;
+    uint4 k8 = make_uint4(0, 0, 0, 0);
+    if (ok) k8 = *reinterpret_cast<const uint4*>(Kb + (int64_t)(p0 + j) * hd + li * 8);
+    const float kf[8] = {bf16_lo(k8.x), bf16_hi(k8.x), bf16_lo(k8.y), bf16_hi(k8.y),
+                         bf16_lo(k8.z), bf16_hi(k8.z), bf16_lo(k8.w), bf16_hi(k8.w)};
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+      const float4 qa = *reinterpret_cast<const float4*>(qs + hh * hd + li * 8);
+      const float4 qb = *reinterpret_cast<const float4*>(qs + hh * hd + li * 8 + 4);
+      float d = qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] +
+                qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
+      for (int o = 1; o < LP; o <<= 1) d += __shfl_xor(d, o, 64);
+      if (ok && li == 0) sc[hh * P.att_maxlen + j] = d * scale;
+    }
+  }
+  __syncthreads();
+  // pass 2: per-head max, exponentials, sums
+  for (int hh = wave; hh < GRP; hh += kWaves) {
+    float m = -INFINITY;
+    for (int j = lane; j < len; j += 64) m = fmaxf(m, sc[hh * P.att_maxlen + j]);
+    m = wave_max(m);
+    float sum = 0.0f;
+    for (int j = lane; j < len; j += 64) {
+      const float p = expf(sc[hh * P.att_maxlen + j] - m);
+      sc[hh * P.att_maxlen + j] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      stats[2 * hh] = m;
+      stats[2 * hh + 1] = sum;
+    }
+  }
+  __syncthreads();
+  // pass 3: sum_j p_j V_j
+  float acc[GRP][8];
+#pragma unroll
+  for (int hh = 0; hh < GRP; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+  for (int jb = wave * PPW; jb < len; jb += kWaves * PPW) {
+    const int j = jb + sub;
+    const bool ok = j < len;
+    uint4 v8 = make_uint4(0, 0, 0, 0);
+    if (ok) v8 = *reinterpret_cast<const uint4*>(Vb + (int64_t)(p0 + j) * hd + li * 8);
+    const float vf[8] = {bf16_lo(v8.x), bf16_hi(v8.x), bf16_lo(v8.y), bf16_hi(v8.y),
+                         bf16_lo(v8.z), bf16_hi(v8.z), bf16_lo(v8.w), bf16_hi(v8.w)};
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) {
+      const float p = ok ? sc[hh * P.att_maxlen + j] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < GRP; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[hh][e];
+      for (int o = LP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      acc[hh][e] = v;
+    }
+  if (sub == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ored[(wave * GRP + hh) * hd + li * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  for (int i = opaque_tid(); i < GRP * hd; i += kThreads) {
+    const int hh = i / hd, e = i - hh * hd;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += ored[(w * GRP + hh) * hd + e];
+    float* dst = P.part + (((int64_t)l * P.nq + h0 + hh) * S + s) * (hd + 2);
+    dst[e] = v;
+    if (e == 0) {
+      dst[hd] = stats[2 * hh];
+      dst[hd + 1] = stats[2 * hh + 1];
+    }
+  }
+  __syncthreads();
+  (void)red;
+}
+
+__device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], g = t.p[1], s = t.p[2], S = t.p[3];
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  if (!vm_wait(P, t, flag)) return false;
+  const int n = P.pos + 1;
+  const int p0 = (int)(((int64_t)s * n) / S), p1 = (int)(((int64_t)(s + 1) * n) / S);
+  const int grp = P.nq / P.nkv, hd = P.hd;
+  if (p1 <= p0) {
+    for (int i = opaque_tid(); i < grp * (hd + 2); i += kThreads) {
+      const int hh = i / (hd + 2), e = i - hh * (hd + 2);
+      float* dst = P.part + (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2);
+      dst[e] = e == hd ? -INFINITY : 0.0f;
+    }
+  } else {
+    for (int h0 = 0; h0 < grp; h0 += 8) {
+      const int nh = min(8, grp - h0);
+      const int hb = g * grp + h0;
+      switch (nh) {
+        case 1: attn_block<1>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 2: attn_block<2>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 3: attn_block<3>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 4: attn_block<4>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 5: attn_block<5>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 6: attn_block<6>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        case 7: attn_block<7>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+        default: attn_block<8>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
+      }
+    }
+  }
+  vm_signal(P, t);
+  return true;
+}
+
+__device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, float* smem) {
+  const int l = t.p[0], h = t.p[1], S = t.p[2];
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  if (!vm_wait(P, t, flag)) return false;
+  const int hd = P.hd;
+  float* wts = smem + P.lds_att;  // S weights
+  float* red = smem;
+  const float* part = P.part + ((int64_t)l * P.nq + h) * S * (hd + 2);
+  // global max of the split maxima
+  float m = -INFINITY;
+  for (int s = opaque_tid(); s < S; s += kThreads) m = fmaxf(m, part[(int64_t)s * (hd + 2) + hd]);
+  m = wave_max(m);
+  if ((opaque_tid() & 63) == 0) red[opaque_tid() >> 6] = m;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int s = opaque_tid(); s < S; s += kThreads) {
+    const float ms = part[(int64_t)s * (hd + 2) + hd];
+    const float wgt = ms == -INFINITY ? 0.0f : expf(ms - M);
+    wts[s] = wgt;
+    lsum += wgt * part[(int64_t)s * (hd + 2) + hd + 1];
+  }
+  const float Ltot = block_sum(lsum, red);  // barrier also publishes wts
+  const float inv = 1.0f / Ltot;
+  for (int e = opaque_tid(); e < hd; e += kThreads) {
+    float v = 0.0f;
+    for (int s = 0; s < S; ++s) v = fmaf(wts[s], part[(int64_t)s * (hd + 2) + e], v);
+    P.o[(int64_t)l * P.nq * hd + (int64_t)h * hd + e] = v * inv;
+  }
+  vm_signal(P, t);
+  return true;
+}
+
+__device__ __forceinline__ bool task_nop(const VmParams& P, const DevTask& t, float* smem) {
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  if (!vm_wait(P, t, flag)) return false;
+  vm_signal(P, t);
+  return true;
+}
+
+template <int DEPTH>
+__global__ void __launch_bounds__(kThreads) amk_vm(VmParams P) {
+  extern __shared__ __align__(16) float smem[];
+  const int q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
+  for (int qi = q0; qi < q1; ++qi) {
+    const DevTask& t = P.tasks[P.queue[qi]];
+    bool ok;
+    switch (t.type) {
+      case AMK_TASK_QKV: ok = task_qkv<DEPTH>(P, t, smem); break;
+      case AMK_TASK_ATTN: ok = task_attn(P, t, smem); break;
+      case AMK_TASK_MERGE: ok = task_merge(P, t, smem); break;
+      case AMK_TASK_OPROJ: ok = task_oproj<DEPTH>(P, t, smem); break;
+      case AMK_TASK_GATEUP: ok = task_gateup<DEPTH>(P, t, smem); break;
+      case AMK_TASK_DOWN: ok = task_down<DEPTH>(P, t, smem); break;
+      case AMK_TASK_LMHEAD: ok = task_lmhead<DEPTH>(P, t, smem); break;
+      default: ok = task_nop(P, t, smem); break;
+    }
+    if (!ok) return;
+  }
+}
+
+template __global__ void amk_vm<4>(VmParams);
+template __global__ void amk_vm<8>(VmParams);
+template __global__ void amk_vm<16>(VmParams);
+
+}  // namespace amk
+
+// =================================================================== engine
+namespace amk {
+namespace {
+
+#define HIP_TRY(call)                                                                          \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess) return fail(AMK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+const void* kernel_for_depth(int depth) {
+  switch (depth) {
+    case 4: return reinterpret_cast<const void*>(&amk_vm<4>);
+    case 8: return reinterpret_cast<const void*>(&amk_vm<8>);
+    default: return reinterpret_cast<const void*>(&amk_vm<16>);
+  }
+}
+
+}  // namespace
+}  // namespace amk
+
+struct amk_engine {
+  amk_model_config model{};
+  amk_schedule_config config{};
+  int device = 0;
+  const void* kernel = nullptr;
+  size_t lds_bytes = 0;
+  amk::VmParams params{};
+  // device allocations owned by the engine
+  std::vector<void*> owned;
+  uint32_t max_prod = 1;
+  int32_t n_counters = 1;
+  int64_t written = 0;  // positions 0..written-1 hold KV rows
+  int64_t steps = 0;
+  int wallclock_khz = 100000;
+};
+
+namespace amk {
+namespace {
+
+template <typename T>
+amk_status dev_alloc(amk_engine* e, T** out, size_t count) {
+  void* p = nullptr;
+  const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+  hipError_t err = hipMalloc(&p, bytes);
+  if (err != hipSuccess) return fail(AMK_ERR_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(err));
+  e->owned.push_back(p);
+  err = hipMemset(p, 0, bytes);
+  if (err != hipSuccess) return fail(AMK_ERR_HIP, std::string("hipMemset: ") + hipGetErrorString(err));
+  *out = static_cast<T*>(p);
+  return AMK_OK;
+}
+
+template <typename T>
+amk_status upload(amk_engine* e, T** out, const std::vector<T>& host) {
+  amk_status st = dev_alloc(e, out, host.size());
+  if (st != AMK_OK) return st;
+  if (!host.empty()) HIP_TRY(hipMemcpy(*out, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice));
+  return AMK_OK;
+}
+
+void free_engine(amk_engine* e) {
+  for (void* p : e->owned) (void)hipFree(p);
+  delete e;
+}
+
+// The kernel derives every address from (type, params) and the standard
+// buffer layout; refuse descriptions it cannot execute exactly as validated.
+amk_status check_executable(const amk_schedule& s) {
+  const std::vector<Buffer> std_buffers = buffer_table(s.model, s.config.attn_splits);
+  if (s.buffers.size() != std_buffers.size())
+    return fail(AMK_ERR_UNSUPPORTED, "buffer table differs from the library layout");
+  for (size_t b = 0; b < std_buffers.size(); ++b)
+    if (s.buffers[b].size != std_buffers[b].size || s.buffers[b].kind != std_buffers[b].kind)
+      return fail(AMK_ERR_UNSUPPORTED, "buffer table differs from the library layout");
+  for (const Task& t : s.tasks) {
+    if ((int)t.waits.size() > kMaxWaits || (int)t.sigs.size() > kMaxSigs)
+      return fail(AMK_ERR_UNSUPPORTED, "a task has more than 4 waits or signals");
+    if ((t.type == AMK_TASK_ATTN && t.p[3] != s.config.attn_splits) ||
+        (t.type == AMK_TASK_MERGE && t.p[2] != s.config.attn_splits))
+      return fail(AMK_ERR_UNSUPPORTED, "attention split count differs from the schedule config");
+  }
+  return AMK_OK;
+}
+
+}  // namespace
+}  // namespace amk
+
+using namespace amk;
+
+extern "C" {
+
+amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out) {
+  if (!s || !bufs || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  amk_verdict v;
+  amk_status st = amk_validate(s, &v);
+  if (st != AMK_OK) return st;  // unsafe schedules never reach the GPU
+  st = check_model(s->model);
+  if (st != AMK_OK) return st;
+  st = check_executable(*s);
+  if (st != AMK_OK) return st;
+  const amk_model_config& m = s->model;
+  const amk_schedule_config& c = s->config;
+  const int32_t npacked = 3 + 6 * m.n_layers;
+  if (!bufs->weights || bufs->n_weights != npacked || !bufs->kv_cache || !bufs->logits)
+    return fail(AMK_ERR_INVALID_ARG, "device buffers: need " + std::to_string(npacked) +
+                                         " packed weights, a KV cache and a logits buffer");
+  for (int32_t k = 0; k < npacked; ++k)
+    if (!bufs->weights[k]) return fail(AMK_ERR_INVALID_ARG, "packed weight " + std::to_string(k) + " is null");
+
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  if (!prop.cooperativeLaunch) return fail(AMK_ERR_UNSUPPORTED, "device lacks cooperative launch");
+
+  amk_engine* e = new (std::nothrow) amk_engine();
+  if (!e) return fail(AMK_ERR_NOMEM, "out of host memory");
+  e->model = m;
+  e->config = c;
+  e->device = dev;
+  auto bail = [&](amk_status code) {
+    free_engine(e);
+    return code;
+  };
+
+  // ---- LDS plan (floats)
+  const int64_t H = m.hidden, F = m.ffn, qd = (int64_t)m.n_heads * m.head_dim, hd = m.head_dim;
+  const int64_t kmax = std::max({H, F, qd});
+  const int64_t xs_floats = ((kmax + 2047) / 2048) * 2048 + ((kmax + 2047) / 2048) * 64;  // x + int4 chunk sums
+  auto max_rows = [](int64_t n, int64_t T) { return (n + T - 1) / T; };
+  const int64_t res_floats = std::max({2 * max_rows((int64_t)(m.n_heads + 2 * m.n_kv_heads) * hd / 2, c.tiles_qkv),
+                                       max_rows(H, c.tiles_o), 2 * max_rows(F, c.tiles_gateup),
+                                       max_rows(H, c.tiles_down), max_rows(m.vocab, c.tiles_lm)});
+  const int64_t grp = m.n_heads / m.n_kv_heads, gb = std::min<int64_t>(grp, 8);
+  const int64_t maxlen = (m.max_ctx + c.attn_splits - 1) / c.attn_splits + 1;
+  const int64_t att_floats = std::max<int64_t>(gb * hd + gb * maxlen + 2 * gb + kWaves * gb * hd, c.attn_splits);
+  const int64_t head = 16;  // block-reduction slots + flag + int8 sum
+  const int64_t lds_x = head, lds_res = lds_x + xs_floats;
+  const int64_t lds_att = head;
+  const int64_t total_floats = std::max(lds_res + ((res_floats + 3) / 4) * 4, lds_att + att_floats);
+  e->lds_bytes = (size_t)total_floats * 4;
+  if (e->lds_bytes > (size_t)prop.sharedMemPerBlock)
+    return (free_engine(e), fail(AMK_ERR_UNSUPPORTED, "schedule needs " + std::to_string(e->lds_bytes) +
+                                                          " bytes of LDS per workgroup; device allows " +
+                                                          std::to_string(prop.sharedMemPerBlock)));
+  e->kernel = kernel_for_depth(c.pipeline_depth);
+  if (e->lds_bytes > 65536) {
+    hipError_t err = hipFuncSetAttribute(e->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds_bytes);
+    if (err != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(err)));
+  }
+  int per_cu = 0;
+  hipError_t oerr = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, e->kernel, kThreads, e->lds_bytes);
+  if (oerr != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(oerr)));
+  if ((int64_t)per_cu * prop.multiProcessorCount < c.num_cus)
+    return bail(fail(AMK_ERR_UNSUPPORTED, std::to_string(c.num_cus) + " queues exceed the " +
+                                              std::to_string(per_cu * prop.multiProcessorCount) +
+                                              " co-resident workgroups of this device"));
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    e->wallclock_khz = khz;
+
+  // ---- device task table
+  std::vector<uint32_t> P = counter_producers(*s);
+  e->max_prod = 1;
+  for (uint32_t p : P) e->max_prod = std::max(e->max_prod, p);
+  e->n_counters = std::max(1, s->n_counters);
+  std::vector<DevTask> dt(s->tasks.size());
+  for (size_t i = 0; i < s->tasks.size(); ++i) {
+    const Task& t = s->tasks[i];
+    DevTask d{};
+    d.type = t.type;
+    d.nwait = (int32_t)t.waits.size();
+    d.nsig = (int32_t)t.sigs.size();
+    std::copy(t.p, t.p + 8, d.p);
+    for (size_t k = 0; k < t.waits.size(); ++k) {
+      d.wctr[k] = t.waits[k].ctr;
+      d.wthr[k] = t.waits[k].thr;
+      d.wprod[k] = P[t.waits[k].ctr];
+    }
+    for (size_t k = 0; k < t.sigs.size(); ++k) d.sctr[k] = t.sigs[k];
+    dt[i] = d;
+  }
+  std::vector<int32_t> qoff(1, 0), queue;
+  for (const auto& q : s->queues) {
+    queue.insert(queue.end(), q.begin(), q.end());
+    qoff.push_back((int32_t)queue.size());
+  }
+  // RoPE table in double, stored fp32: (cos, sin)(pos * theta^(-2i/hd))
+  const int64_t half = hd / 2;
+  std::vector<float2> rope((size_t)m.max_ctx * half);
+  for (int64_t p = 0; p < m.max_ctx; ++p)
+    for (int64_t i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)m.rope_theta, -2.0 * (double)i / (double)hd);
+      rope[p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  std::vector<const uint8_t*> wptr(npacked);
+  for (int32_t k = 0; k < npacked; ++k) wptr[k] = static_cast<const uint8_t*>(bufs->weights[k]);
+
+  VmParams& pr = e->params;
+  DevTask* d_tasks = nullptr;
+  int32_t *d_qoff = nullptr, *d_queue = nullptr;
+  const uint8_t** d_wptr = nullptr;
+  float2* d_rope = nullptr;
+  if ((st = upload(e, &d_tasks, dt)) != AMK_OK || (st = upload(e, &d_qoff, qoff)) != AMK_OK ||
+      (st = upload(e, &d_queue, queue)) != AMK_OK || (st = upload(e, &d_wptr, wptr)) != AMK_OK ||
+      (st = upload(e, &d_rope, rope)) != AMK_OK)
+    return bail(st);
+  const int64_t L = m.n_layers, S = c.attn_splits;
+  if ((st = dev_alloc(e, &pr.x, (size_t)(L * 2 * H))) != AMK_OK ||
+      (st = dev_alloc(e, &pr.q, (size_t)(L * qd))) != AMK_OK ||
+      (st = dev_alloc(e, &pr.part, (size_t)(L * m.n_heads * S * (hd + 2)))) != AMK_OK ||
+      (st = dev_alloc(e, &pr.o, (size_t)(L * qd))) != AMK_OK ||
+      (st = dev_alloc(e, &pr.a, (size_t)(L * F))) != AMK_OK ||
+      (st = dev_alloc(e, &pr.ctr, (size_t)std::max(1, s->n_counters) * kCounterStride)) != AMK_OK ||
+      (st = dev_alloc(e, &pr.err, 64)) != AMK_OK)
+    return bail(st);
+  pr.tasks = d_tasks;
+  pr.queue_off = d_qoff;
+  pr.queue = d_queue;
+  pr.wptr = d_wptr;
+  pr.rope = d_rope;
+  pr.kv = static_cast<uint16_t*>(bufs->kv_cache);
+  pr.logits = bufs->logits;
+  pr.L = m.n_layers;
+  pr.H = m.hidden;
+  pr.nq = m.n_heads;
+  pr.nkv = m.n_kv_heads;
+  pr.hd = m.head_dim;
+  pr.F = m.ffn;
+  pr.V = m.vocab;
+  pr.mc = m.max_ctx;
+  pr.S = c.attn_splits;
+  pr.wfmt = m.wfmt;
+  pr.act_bf16 = m.act_bf16;
+  pr.eps = m.rms_eps;
+  pr.lds_x = (int32_t)lds_x;
+  pr.lds_res = (int32_t)lds_res;
+  pr.lds_att = (int32_t)lds_att;
+  pr.att_maxlen = (int32_t)maxlen;
+  pr.spin_ticks = (uint64_t)2000000 * (uint64_t)e->wallclock_khz / 1000u;
+  *out = e;
+  return AMK_OK;
+}
+
+amk_status amk_decode_step(amk_engine* e, int32_t token, int32_t pos, void* stream) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  if (token < 0 || token >= e->model.vocab) return fail(AMK_ERR_OUT_OF_RANGE, "token out of range");
+  if (pos < 0 || pos >= e->model.max_ctx) return fail(AMK_ERR_OUT_OF_RANGE, "pos out of range");
+  if (pos > e->written)
+    return fail(AMK_ERR_INVALID_ARG, "pos " + std::to_string(pos) + " leaves a gap: only " +
+                                         std::to_string(e->written) + " positions are written");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // counters are monotonic across launches; restart them well before u32 wraps
+  if ((uint64_t)(e->params.epoch + 2) * e->max_prod >= (1ull << 31)) {
+    HIP_TRY(hipMemsetAsync(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
+    e->params.epoch = 0;
+  }
+  e->params.token = token;
+  e->params.pos = pos;
+  void* args[] = {&e->params};
+  HIP_TRY(hipLaunchCooperativeKernel(e->kernel, dim3(e->config.num_cus), dim3(kThreads), args,
+                                     (unsigned)e->lds_bytes, st));
+  e->params.epoch += 1;
+  e->written = (int64_t)pos + 1;
+  e->steps += 1;
+  return AMK_OK;
+}
+
+amk_status amk_engine_check(amk_engine* e) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  int32_t err = 0;
+  HIP_TRY(hipMemcpy(&err, e->params.err, sizeof(err), hipMemcpyDeviceToHost));
+  if (err != 0) {
+    // counters of an aborted launch are inconsistent: restart from zero
+    HIP_TRY(hipMemset(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters));
+    HIP_TRY(hipMemset(e->params.err, 0, sizeof(int32_t)));
+    e->params.epoch = 0;
+    return fail(AMK_ERR_TIMEOUT, "a device-side wait exceeded its spin budget");
+  }
+  return AMK_OK;
+}
+
+amk_status amk_engine_set_kv_length(amk_engine* e, int32_t n) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  if (n < 0 || n > e->model.max_ctx) return fail(AMK_ERR_OUT_OF_RANGE, "kv length out of range");
+  e->written = n;
+  return AMK_OK;
+}
+
+amk_status amk_engine_set_spin_budget(amk_engine* e, int64_t us) {
+  if (!e || us <= 0) return fail(AMK_ERR_INVALID_ARG, "bad engine or budget");
+  e->params.spin_ticks = (uint64_t)us * (uint64_t)e->wallclock_khz / 1000u;
+  return AMK_OK;
+}
+
+amk_status amk_engine_steps(const amk_engine* e, int64_t* out) {
+  if (!e || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  *out = e->steps;
+  return AMK_OK;
+}
+
+amk_status amk_engine_destroy(amk_engine* e) {
+  if (!e) return AMK_OK;
+  free_engine(e);
+  return AMK_OK;
+}
+
+}  // extern "C"
