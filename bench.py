@@ -1,0 +1,217 @@
+"""Batch-1 decode benchmark of the persistent megakernel on one MI355X.
+
+One "step" is one decode step of the whole model (one cooperative launch):
+token in, logits out, KV row written.  The workload is the ~8B Llama-shaped
+bf16 decoder (32 layers, hidden 4096, 32/8 heads x 128, FFN 14336, vocab
+128256) with a 1024-token prompt already in the KV cache and 256 decode
+steps, on seeded random N(0, 0.02) weights (synthetic data; no checkpoint).
+
+Reported: decode tokens/s (value), per-step latency, and the fraction of the
+latency floor t_min(p) = B(p) / 8.0e12 B/s, where B(p) = every stored weight
+byte (projections, scales, norms, LM head) + one embedding row + the KV
+bytes of positions 0..p + the fp32 logits.  The `roofline` object gives the
+achieved algorithmic GB/s of the single kernel (amk_vm) per launch, timed
+with HIP events on the launch stream.  `cpu_baseline` times the oracle on a
+bounded sample of the same workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12  # bytes/s, MI355X published HBM3E bandwidth
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "persistent_megakernel_wg_amd", "csrc", "vm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(amk, model, pos):
+    """Algorithmic bytes of the decode step at position pos (see module doc)."""
+    H, V, L = model.hidden, model.vocab, model.n_layers
+    n = amk.packed_count(model)
+    weights = sum(amk.packed_bytes(model, k) for k in range(1, n))  # all but the embedding table
+    emb_row = 2 * H
+    kv = L * 2 * model.n_kv_heads * model.head_dim * 2 * (pos + 1)
+    return weights + emb_row + kv + 4 * V
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, nsteps_bytes):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"traffic_amk_vm_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, weights, budget_s=20.0, max_steps=8):
+    """Oracle decode steps at the prompt's context length on this host."""
+    import oracle
+    kvp = None
+    m = oracle.Model(wl, weights)
+    kv = m.new_kv()
+    P = wl.prompt_len
+    # the prompt's KV rows: synthetic (oracle cost does not depend on values)
+    import synth
+    if P > 0:
+        kvp = synth.kv_prefix(wl, P, seed=3)
+        kv[...] = kvp
+    toks = synth.tokens(2, P + max_steps, wl.vocab)[P:]
+    times = []
+    t_start = time.time()
+    for i, tok in enumerate(toks):
+        t0 = time.time()
+        m.step(kv, int(tok), P + i)
+        times.append(time.time() - t0)
+        if time.time() - t_start > budget_s:
+            break
+    m.close()
+    per = float(np.mean(times))
+    return {"value": 1.0 / per, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(times)} decode steps at positions {P}..{P + len(times) - 1} of the "
+                      f"{wl.name} workload (prompt KV rows filled with seeded values), "
+                      f"{per * 1e3:.0f} ms/step, double-precision C++ oracle with OpenMP over output rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default: workload's)")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed decode steps after the prompt")
+    ap.add_argument("--workload", default="8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--depth", type=int, default=0, help="pipeline_depth override")
+    ap.add_argument("--sched", default="", help="schedule overrides k=v,k=v")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path is a "
+              "single-GPU persistent kernel; multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import persistent_megakernel_wg_amd as amk
+    import synth
+
+    wl = synth.get(args.workload)
+    steps = args.steps if args.steps is not None else wl.decode_steps
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    model = amk.ModelConfig.from_workload(wl)
+    cfg = amk.default_schedule_config(model, cus)
+    if args.depth:
+        cfg.pipeline_depth = args.depth
+    for kv_ in filter(None, args.sched.split(",")):
+        k, v = kv_.split("=")
+        setattr(cfg, k, int(v))
+    sched = amk.Schedule.build(model, cfg)
+    verdict = sched.validate()
+    assert verdict[0] == 0, verdict
+
+    t0 = time.time()
+    weights = synth.model_weights(wl, seed=1)
+    log(f"generated {wl.name} weights in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    dev_w = amk.upload_model(model, weights, device=dev)
+    log(f"packed + uploaded in {time.time() - t0:.1f}s "
+        f"({sum(w.numel() for w in dev_w) / 1e9:.2f} GB on device)")
+    kv, logits = amk.alloc_state(model, device=dev)
+    eng = amk.Engine(sched, dev_w, kv, logits)
+    toks = synth.tokens(2, wl.prompt_len + steps + args.warmup, wl.vocab)
+    stream = torch.cuda.current_stream()
+
+    # prompt: teacher-forced decode steps (untimed)
+    t0 = time.time()
+    for p in range(wl.prompt_len):
+        eng.decode_step(int(toks[p]), p, stream)
+    torch.cuda.synchronize()
+    eng.check()
+    log(f"prompt of {wl.prompt_len} positions in {time.time() - t0:.2f}s")
+    P = wl.prompt_len
+    # warmup steps, then rewind so that the timed steps see the workload's positions
+    for i in range(args.warmup):
+        eng.decode_step(int(toks[P + i]), P + i, stream)
+    torch.cuda.synchronize()
+    eng.check()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    dec = toks[P + args.warmup:]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        eng.decode_step(int(dec[i]), P + i, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    eng.check()
+    lat = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)])  # seconds
+    gpu_total = float(lat.sum())
+    B = np.array([step_bytes(amk, model, P + i) for i in range(steps)], dtype=np.float64)
+    tmin = B / HBM_PEAK
+    floor_frac = float(tmin.sum() / gpu_total)
+    achieved = float(B.mean() / lat.mean())
+    traffic = load_traffic(wl.name, B.mean())
+    out = {
+        "metric": "batch-1 decode tokens/s and % of weight+KV bytes / HBM-BW latency floor",
+        "value": steps / t_total,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_total / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.wfmt if wl.wfmt != "bf16" else "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, seeded uniform tokens)",
+        "config": {"workload": f"{wl.name}: {wl.n_layers} layers, hidden {wl.hidden}, "
+                               f"{wl.n_heads}/{wl.n_kv_heads} heads x {wl.head_dim}, FFN {wl.ffn}, "
+                               f"vocab {wl.vocab}, {wl.wfmt} weights, batch 1, "
+                               f"{wl.prompt_len}-token prompt, decode positions {P}..{P + steps - 1}",
+                   "batch": 1, "prompt_len": P, "decode_steps": steps,
+                   "schedule": cfg.as_dict()},
+        "floor_fraction": floor_frac,
+        "t_min_ms_mean": float(tmin.mean() * 1e3),
+        "latency_ms": {"mean": float(lat.mean() * 1e3), "median": float(np.median(lat) * 1e3),
+                       "p90": float(np.percentile(lat, 90) * 1e3), "min": float(lat.min() * 1e3)},
+        "bytes_per_step_mean": float(B.mean()),
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    del eng
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl, weights, budget_s=args.cpu_budget)
+        log(f"cpu baseline in {time.time() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

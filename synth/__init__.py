@@ -31,7 +31,7 @@ def build():
     """Compile libsynth.so (plain C, OpenMP)."""
     src = os.path.join(_HERE, "gen.c")
     tmp = _LIB_PATH + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, src, "-lm"])
+    subprocess.check_call(["gcc", "-O2", "-fno-math-errno", "-fopenmp", "-shared", "-fPIC", "-o", tmp, src, "-lm"])
     os.replace(tmp, _LIB_PATH)
 
 

@@ -52,17 +52,22 @@ void synth_normal_bf16(uint64_t seed, uint64_t stream, double stdev,
   const uint64_t key = stream_key(seed, stream);
   const double two_pi = 6.283185307179586476925286766559;
   const double inv53 = 1.0 / 9007199254740992.0; /* 2^-53 */
-  long long i;
+  if (n == 0) return;
+  /* pairs j0..j1 cover elements first..first+n-1; both outputs of a pair
+     are computed together and stored when inside the range */
+  const uint64_t j0 = first >> 1, j1 = (first + n - 1) >> 1;
+  long long jj;
 #pragma omp parallel for schedule(static)
-  for (i = 0; i < (long long)n; ++i) {
-    uint64_t e = first + (uint64_t)i;
-    uint64_t j = e >> 1;
+  for (jj = (long long)j0; jj <= (long long)j1; ++jj) {
+    uint64_t j = (uint64_t)jj;
     uint64_t r1 = sm(key + 2 * j), r2 = sm(key + 2 * j + 1);
     double u1 = (double)((r1 >> 11) + 1) * inv53;
     double u2 = (double)(r2 >> 11) * inv53;
     double rad = sqrt(-2.0 * log(u1));
-    double z = (e & 1) ? rad * sin(two_pi * u2) : rad * cos(two_pi * u2);
-    out[i] = f32_to_bf16_rne((float)(stdev * z));
+    double ang = two_pi * u2;
+    uint64_t e0 = 2 * j, e1 = 2 * j + 1;
+    if (e0 >= first && e0 < first + n) out[e0 - first] = f32_to_bf16_rne((float)(stdev * rad * cos(ang)));
+    if (e1 >= first && e1 < first + n) out[e1 - first] = f32_to_bf16_rne((float)(stdev * rad * sin(ang)));
   }
 }
 

@@ -28,3 +28,46 @@ def test_tiny_full_protocol():
     g = (kv_g[..., :n, :].astype(np.uint32) << 16).view(np.float32)
     o = (kv_o[..., :n, :].astype(np.uint32) << 16).view(np.float32)
     assert np.allclose(g, o, rtol=2 ** -7, atol=1e-6)
+
+
+@pytest.fixture(scope="module")
+def w8b():
+    wl = synth.get("8b")
+    log("generating 8b weights")
+    return synth.model_weights(wl, seed=1)
+
+
+def _free():
+    import gc
+
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["8b"])
+def test_full_size_short_prompt(name, w8b):
+    """Full-size model, launch configuration of the bench: a 3-token prompt
+    and 3 decode steps, every step compared with the oracle."""
+    wl = synth.get(name)
+    toks = synth.tokens(2, 6, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w8b, toks)
+    del eng
+    _free()
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"{name} short: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+@pytest.mark.parametrize("name", ["8b"])
+def test_full_size_long_context(name, w8b):
+    """Full-size model after the workload's prompt length: the KV cache holds
+    seeded rows 0..P-1 (same bytes on both sides), then 2 decode steps."""
+    wl = synth.get(name)
+    P = wl.prompt_len
+    kvp = synth.kv_prefix(wl, P, seed=3)
+    toks = synth.tokens(2, P + 2, wl.vocab)[P:]
+    res, eng, _ = teacher_forced(wl, w8b, toks, kv_prefix=kvp, start=P)
+    del eng
+    _free()
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"{name} long: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
