@@ -94,6 +94,49 @@ def cpu_baseline(wl, weights, budget_s=20.0, max_steps=8):
                       f"{per * 1e3:.0f} ms/step, double-precision C++ oracle with OpenMP over output rows"}
 
 
+def analyse_trace(view, stamps, khz):
+    """Wait share and per-join latency of one traced launch.
+
+    stamps[i] = (wait begin, wait end, work end, signal end) of task i."""
+    us = 1e3 / khz
+    st = stamps.astype(np.int64)
+    t0 = st[:, 0].min()
+    st = (st - t0) * us
+    wait = st[:, 1] - st[:, 0]
+    work = st[:, 2] - st[:, 1]
+    sig = st[:, 3] - st[:, 2]
+    tasks = view["tasks"]
+    types = np.array([t["type"] for t in tasks])
+    names = ["NOP", "QKV", "ATTN", "MERGE", "OPROJ", "GATEUP", "DOWN", "LMHEAD"]
+    per_type = {}
+    for ty in sorted(set(types.tolist())):
+        m = types == ty
+        per_type[names[ty]] = {"n": int(m.sum()), "wait_us": float(wait[m].mean()),
+                               "work_us": float(work[m].mean()), "signal_us": float(sig[m].mean())}
+    # join latency: last producer's signal end -> consumers' wait end
+    prod = {}
+    for i, t in enumerate(tasks):
+        for c in t["sigs"]:
+            prod.setdefault(c, []).append(i)
+    lat_first, lat_med = [], []
+    for i, t in enumerate(tasks):
+        pass
+    cons = {}
+    for i, t in enumerate(tasks):
+        for c, _ in t["waits"]:
+            cons.setdefault(c, []).append(i)
+    for c, ws in cons.items():
+        last = max(st[p, 3] for p in prod[c])
+        wake = np.array([st[w, 1] for w in ws])
+        lat_first.append(wake.min() - last)
+        lat_med.append(np.median(wake) - last)
+    span = float(st[:, 3].max())
+    return {"span_us": span, "wait_share": float(wait.sum() / (st[:, 3] - st[:, 0]).sum()),
+            "join_latency_us": {"first_waiter_mean": float(np.mean(lat_first)),
+                                "median_waiter_mean": float(np.mean(lat_med))},
+            "per_type": per_type}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +147,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--depth", type=int, default=0, help="pipeline_depth override")
     ap.add_argument("--sched", default="", help="schedule overrides k=v,k=v")
+    ap.add_argument("--trace", default="", help="after timing, trace 2 steps and write the analysis here")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path is a "
@@ -205,6 +249,20 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if args.trace:
+        eng.set_trace(True)
+        for i in range(2):
+            eng.decode_step(int(dec[i]), P + i, stream)
+        torch.cuda.synchronize()
+        eng.check()
+        eng.set_trace(False)
+        view = sched.view()
+        stamps, khz = eng.read_trace(len(view["tasks"]))
+        tr = analyse_trace(view, stamps, khz)
+        with open(args.trace, "w") as f:
+            json.dump(tr, f, indent=1)
+        out["trace"] = {k: tr[k] for k in ("span_us", "wait_share", "join_latency_us")}
+        log(f"trace: {json.dumps(tr)}")
     del eng
     if not args.no_cpu_baseline:
         t0 = time.time()

@@ -266,10 +266,30 @@ amk_status amk_engine_check(amk_engine* engine);
  * the launch then drains; amk_engine_check reports it. */
 amk_status amk_engine_set_spin_budget(amk_engine* engine, int64_t microseconds);
 
+/* Per-task timing of the following launches (the region timing of the Argus
+ * page's megakernel case study, section "Case 3": device-side timestamps of
+ * the intervals between phases).  With tracing on, thread 0 of each
+ * workgroup stores four wall-clock stamps per task: wait begin, wait end
+ * (counters reached, acquire done), work end, signal end.  Off by default;
+ * the stamps cost a few scalar instructions per task. */
+amk_status amk_engine_set_trace(amk_engine* engine, int32_t enable);
+
+/* Copy the stamps of the last traced launch: out[4*task + k], n_values =
+ * 4 * n_tasks; *clock_khz receives the stamp clock rate. */
+amk_status amk_engine_read_trace(amk_engine* engine, uint64_t* out, int64_t n_values,
+                                 int32_t* clock_khz);
+
 /* Host-side count of decode steps since creation (for the caller's bookkeeping). */
 amk_status amk_engine_steps(const amk_engine* engine, int64_t* out);
 
 amk_status amk_engine_destroy(amk_engine* engine);
+
+/* Measurement utility, not part of the decode path: one plain streaming-read
+ * launch over `bytes` (a multiple of 16) of device memory `src`, `blocks`
+ * workgroups of 256 threads, one float per block written to device `out`
+ * (blocks floats).  Enqueued on hip_stream; time it with events. */
+amk_status amk_stream_read_probe(const void* src, size_t bytes, float* out, int32_t blocks,
+                                 void* hip_stream);
 
 /* ---- errors ------------------------------------------------------------------ */
 

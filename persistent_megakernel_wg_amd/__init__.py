@@ -119,8 +119,11 @@ _SIGS = {
     "amk_engine_check": ([_p], _i32),
     "amk_engine_set_spin_budget": ([_p, _i64], _i32),
     "amk_engine_set_kv_length": ([_p, _i32], _i32),
+    "amk_engine_set_trace": ([_p, _i32], _i32),
+    "amk_engine_read_trace": ([_p, _p, _i64, ctypes.POINTER(_i32)], _i32),
     "amk_engine_steps": ([_p, ctypes.POINTER(_i64)], _i32),
     "amk_engine_destroy": ([_p], _i32),
+    "amk_stream_read_probe": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
     "amk_status_string": ([_i32], ctypes.c_char_p),
     "amk_last_error": ([], ctypes.c_char_p),
 }
@@ -388,6 +391,17 @@ class Engine:
     def set_kv_length(self, n):
         _check(_lib.amk_engine_set_kv_length(self._h, int(n)), "amk_engine_set_kv_length")
 
+    def set_trace(self, enable):
+        _check(_lib.amk_engine_set_trace(self._h, int(bool(enable))), "amk_engine_set_trace")
+
+    def read_trace(self, n_tasks):
+        """(stamps uint64 [n_tasks][4], clock kHz) of the last traced launch."""
+        out = np.empty((n_tasks, 4), dtype=np.uint64)
+        khz = _i32()
+        _check(_lib.amk_engine_read_trace(self._h, out.ctypes.data, out.size, ctypes.byref(khz)),
+               "amk_engine_read_trace")
+        return out, khz.value
+
     def set_spin_budget(self, microseconds):
         _check(_lib.amk_engine_set_spin_budget(self._h, int(microseconds)), "amk_engine_set_spin_budget")
 
@@ -406,6 +420,16 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+def stream_read_probe(src, out, blocks, stream=None):
+    """Enqueue one plain streaming read of tensor `src` (see amk.h)."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.amk_stream_read_probe(ctypes.c_void_p(src.data_ptr()), nbytes - nbytes % 16,
+                                      ctypes.c_void_p(out.data_ptr()), int(blocks),
+                                      ctypes.c_void_p(s.cuda_stream)), "amk_stream_read_probe")
 
 
 def upload_model(model, canonical, device="cuda"):

@@ -122,7 +122,7 @@ constexpr int kMaxSigs = 4;
 constexpr int kCounterStride = 32;  // u32 per counter: one 128-byte line each
 
 struct alignas(16) DevTask {
-  int32_t type, nwait, nsig, pad0;
+  int32_t type, nwait, nsig, id;
   int32_t p[8];
   int32_t wctr[kMaxWaits];
   uint32_t wthr[kMaxWaits];

@@ -17,12 +17,11 @@ amk_status check_model(const amk_model_config& m) {
     return fail(AMK_ERR_UNSUPPORTED, "biased projections are not supported");
   if (m.n_heads % m.n_kv_heads)
     return fail(AMK_ERR_UNSUPPORTED, "n_heads must be a multiple of n_kv_heads");
-  if (m.head_dim % 8 || m.head_dim > 256)
-    return fail(AMK_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and at most 256");
+  if (m.head_dim != 64 && m.head_dim != 128 && m.head_dim != 256)
+    return fail(AMK_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
   if (m.n_heads / m.n_kv_heads > 16)
     return fail(AMK_ERR_UNSUPPORTED, "at most 16 query heads per kv head");
-  if (std::min(8, m.n_heads / m.n_kv_heads) * m.head_dim > 1024)
-    return fail(AMK_ERR_UNSUPPORTED, "min(8, query heads per kv head) * head_dim must be at most 1024");
+
   if (m.wfmt < AMK_W_BF16 || m.wfmt > AMK_W_INT4_G128)
     return fail(AMK_ERR_UNSUPPORTED, "unknown weight format");
   const int64_t qdim = (int64_t)m.n_heads * m.head_dim;

@@ -50,6 +50,7 @@ struct VmParams {
   float* a;     // [L][F]
   uint32_t* ctr;
   int32_t* err;
+  uint64_t* trace;  // null, or 4 wall-clock stamps per task (see vm_wait / vm_signal)
   const float2* rope;  // [mc][hd/2] (cos, sin)
   uint64_t spin_ticks;
   int32_t token, pos;
@@ -83,14 +84,64 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(bf16_bits(f) << 16); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane reductions on the VALU with DPP (no LDS crossbar round trips).
+// dpp<CTRL, ROWMASK>(old, v): lanes of rows outside ROWMASK keep `old`.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWMASK, 0xF, false));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+constexpr int kHalfMirror = 0x141, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// every lane of each 16-lane row gets the row's sum
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kRowRor8>(0.0f, v);
+  v += dpp<kRowRor4>(0.0f, v);
+  v += dpp<kQuadSwap2>(0.0f, v);
+  v += dpp<kQuadSwap1>(0.0f, v);
   return v;
 }
+// every lane of each 8-lane half row gets the half row's sum
+__device__ __forceinline__ float row_sum8(float v) {
+  v += dpp<kHalfMirror>(0.0f, v);
+  v += dpp<kQuadSwap2>(0.0f, v);
+  v += dpp<kQuadSwap1>(0.0f, v);
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kRowRor8>(v, v));
+  v = fmaxf(v, dpp<kRowRor4>(v, v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v, v));
+  v = fmaxf(v, dpp<kQuadSwap1>(v, v));
+  return v;
+}
+// sum over the 64 lanes, returned uniformly (row sums, then the row
+// broadcasts carry rows 0..2 into row 3, then lane 63 is read)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += dpp<kRowBcast15, 0xA>(0.0f, v);
+  v += dpp<kRowBcast31, 0xC>(0.0f, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = row_max16(v);
+  v = fmaxf(v, dpp<kRowBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp<kRowBcast31, 0xC>(v, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// sum over groups of LG consecutive lanes (LG = 8, 16, 32 or 64), every lane
+// of a group gets its group's sum
+template <int LG>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LG == 8) return row_sum8(v);
+  if constexpr (LG == 16) return row_sum16(v);
+  if constexpr (LG == 32) {
+    v = row_sum16(v);
+    return v + __shfl_xor(v, 16, 64);
+  }
+  if constexpr (LG == 64) return wave_sum(v);
   return v;
 }
 
@@ -112,6 +163,17 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Stores of data another workgroup reads in the same launch go through at
+// agent scope (written through to the device coherence point), so that a
+// signal only has to wait for its own stores to complete instead of writing
+// back the whole L2 of its XCD.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufFlags);
 }
@@ -130,6 +192,7 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // workgroup already reported an error (the launch then drains).
 __device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int* flag) {
   if (opaque_tid() == 0) {
+    if (P.trace) P.trace[(size_t)t.id * 4 + 0] = wall_clock64();
     int ok = 1;
     for (int k = 0; k < t.nwait && ok; ++k) {
       const uint32_t target = P.epoch * t.wprod[k] + t.wthr[k];
@@ -150,20 +213,25 @@ __device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int
     if (!ok) __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag = ok;
+    if (P.trace) P.trace[(size_t)t.id * 4 + 1] = wall_clock64();
   }
   __syncthreads();
   return *flag != 0;
 }
 
-// All threads' stores are ordered before the barrier; thread 0 then
-// releases at agent scope and bumps each counter once.
+// Release: every wave waits until its own stores have completed (all data
+// read by other workgroups is written with agent-scope stores, so completion
+// means visible at the device coherence point), the barrier joins the waves,
+// then thread 0 bumps each counter once with a relaxed agent-scope add.
 __device__ __forceinline__ void vm_signal(const VmParams& P, const DevTask& t) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (opaque_tid() == 0 && t.nsig > 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (opaque_tid() == 0) {
+    if (P.trace) P.trace[(size_t)t.id * 4 + 2] = wall_clock64();
     for (int k = 0; k < t.nsig; ++k)
       __hip_atomic_fetch_add(P.ctr + (size_t)t.sctr[k] * kCounterStride, 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
+    if (P.trace) P.trace[(size_t)t.id * 4 + 3] = wall_clock64();
   }
 }
 
@@ -650,13 +718,13 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, fl
     }
     if (hs < nq) {
       float* qd = P.q + (int64_t)l * nq * hd + (int64_t)hs * hd;
-      qd[i] = a;
-      qd[i + half] = b;
+      st_agent(qd + i, a);
+      st_agent(qd + i + half, b);
     } else {
       const int kvsel = hs < nq + nkv ? 0 : 1, g = hs - nq - kvsel * nkv;
       uint16_t* row = P.kv + ((((int64_t)l * 2 + kvsel) * nkv + g) * P.mc + P.pos) * hd;
-      row[i] = (uint16_t)bf16_bits(a);
-      row[i + half] = (uint16_t)bf16_bits(b);
+      st_agent(row + i, (uint16_t)bf16_bits(a));
+      st_agent(row + i + half, (uint16_t)bf16_bits(b));
     }
   }
   vm_signal(P, t);
@@ -677,7 +745,7 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, 
     float resid;
     if (l == 0) resid = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
     else resid = P.x[((int64_t)(l - 1) * 2 + 1) * H + r];
-    dst[r] = resid + res[k];
+    st_agent(dst + r, resid + res[k]);
   }
   vm_signal(P, t);
   return true;
@@ -696,7 +764,7 @@ __device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t,
   float* dst = P.a + (int64_t)l * F;
   for (int k = opaque_tid(); k < j1 - j0; k += kThreads) {
     const float g = res[2 * k], u = res[2 * k + 1];
-    dst[j0 + k] = g / (1.0f + expf(-g)) * u;
+    st_agent(dst + j0 + k, g / (1.0f + expf(-g)) * u);
   }
   vm_signal(P, t);
   return true;
@@ -712,7 +780,7 @@ __device__ __forceinline__ bool task_down(const VmParams& P, const DevTask& t, f
   const float* res = smem + P.lds_res;
   const float* mid = P.x + (int64_t)l * 2 * H;
   float* dst = P.x + ((int64_t)l * 2 + 1) * H;
-  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) dst[r0 + k] = mid[r0 + k] + res[k];
+  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) st_agent(dst + r0 + k, mid[r0 + k] + res[k]);
   vm_signal(P, t);
   return true;
 }
@@ -731,176 +799,259 @@ __device__ __forceinline__ bool task_lmhead(const VmParams& P, const DevTask& t,
   return true;
 }
 
-// One split of the positions of kv head g for its GRP query heads.
-// Partials: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
-template <int GRP>
-__device__ __forceinline__ void attn_block(const VmParams& P, int l, int g, int h0, int s, int S, int p0, int len,
-                           float* smem) {
-  const int hd = P.hd, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int LP = hd >> 3, PPW = 64 / LP, sub = lane / LP, li = lane - sub * LP;
-  float* red = smem;
-  float* qs = smem + P.lds_att;                 // GRP*hd
-  float* sc = qs + GRP * hd;                    // GRP*maxlen
-  float* stats = sc + GRP * P.att_maxlen;       // 2*GRP
-  float* ored = stats + 2 * GRP;                // kWaves*GRP*hd
+// ------------------------------------------------------------ attention --
+// One split [p0, p1) of the positions of kv head g, for query heads
+// h0..h0+nh-1 (nh <= GP).  Lane layout ("head rows"): LH = hd/8 lanes hold the
+// 8-element chunks of one row; GP groups of LH lanes take GP query heads; the
+// remaining factor PW = 64/(LH*GP) takes PW positions per wave step.  Chunk c
+// of block b of wave w is position p0 + ((b*MAXC + c)*8 + w)*PW + lane/(LH*GP).
+// A score needs one LH-lane DPP sum; the online softmax and sum p*V stay in
+// each lane (every lane of a group holds its group's max and sum), and the
+// (wave, position group) states are merged once through LDS.  Rows of
+// earlier positions were written by previous launches, so block 0 is loaded
+// before the wait; the row at `pos` (written by this launch) is re-read after.
+// Output: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
+template <int LH, int GP, int MAXC>
+__device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, int l, int g, int h0,
+                                           int nh, int s, int S, int p0, int p1, float* smem) {
+  constexpr int PW = 64 / (LH * GP);
+  const int hd = P.hd, pos = P.pos, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int pw = lane / (LH * GP), hh = (lane / LH) % GP, li = lane % LH;
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  const uint16_t* Kb = P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd + li * 8;
+  const uint16_t* Vb = P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd + li * 8;
+  auto posof = [&](int blk, int c) { return p0 + ((blk * MAXC + c) * kWaves + wave) * PW + pw; };
+  uint4 kr[MAXC], vr[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int j = posof(0, c);
+    const bool ok = j < p1 && j < pos;
+    kr[c] = ok ? *reinterpret_cast<const uint4*>(Kb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+    vr[c] = ok ? *reinterpret_cast<const uint4*>(Vb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+  }
+  if (!vm_wait(P, t, flag)) return false;
+  const bool hv = hh < nh;
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int i = opaque_tid(); i < GRP * hd; i += kThreads)
-    qs[i] = P.q[(int64_t)l * P.nq * hd + (int64_t)h0 * hd + i];
-  __syncthreads();
-  const uint16_t* Kb = P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd;
-  const uint16_t* Vb = P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd;
-  // pass 1: scores
-  for (int jb = wave * PPW; jb < len; jb += kWaves * PPW) {
-    const int j = jb + sub;
-    const bool ok = j < len;
-    uint4 k8 = make_uint4(0, 0, 0, 0);
-    if (ok) k8 = *reinterpret_cast<const uint4*>(Kb + (int64_t)(p0 + j) * hd + li * 8);
-    const float kf[8] = {bf16_lo(k8.x), bf16_hi(k8.x), bf16_lo(k8.y), bf16_hi(k8.y),
-                         bf16_lo(k8.z), bf16_hi(k8.z), bf16_lo(k8.w), bf16_hi(k8.w)};
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-      const float4 qa = *reinterpret_cast<const float4*>(qs + hh * hd + li * 8);
-      const float4 qb = *reinterpret_cast<const float4*>(qs + hh * hd + li * 8 + 4);
-      float d = qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] +
-                qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
-      for (int o = 1; o < LP; o <<= 1) d += __shfl_xor(d, o, 64);
-      if (ok && li == 0) sc[hh * P.att_maxlen + j] = d * scale;
-    }
+  float q[8];
+  {
+    const float* qp = P.q + (int64_t)l * P.nq * hd + (int64_t)(h0 + (hv ? hh : 0)) * hd + li * 8;
+    const float4 a = *reinterpret_cast<const float4*>(qp);
+    const float4 b = *reinterpret_cast<const float4*>(qp + 4);
+    q[0] = a.x * scale; q[1] = a.y * scale; q[2] = a.z * scale; q[3] = a.w * scale;
+    q[4] = b.x * scale; q[5] = b.y * scale; q[6] = b.z * scale; q[7] = b.w * scale;
   }
-  __syncthreads();
-  // pass 2: per-head max, exponentials, sums
-  for (int hh = wave; hh < GRP; hh += kWaves) {
-    float m = -INFINITY;
-    for (int j = lane; j < len; j += 64) m = fmaxf(m, sc[hh * P.att_maxlen + j]);
-    m = wave_max(m);
-    float sum = 0.0f;
-    for (int j = lane; j < len; j += 64) {
-      const float p = expf(sc[hh * P.att_maxlen + j] - m);
-      sc[hh * P.att_maxlen + j] = p;
-      sum += p;
+  float M = -INFINITY, Ls = 0.0f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  const int len = p1 - p0;
+  const int per_blk = MAXC * kWaves * PW;
+  const int nblk = (len + per_blk - 1) / per_blk;
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (blk > 0) {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int j = posof(blk, c);
+        const bool ok = j < p1;
+        kr[c] = ok ? *reinterpret_cast<const uint4*>(Kb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+        vr[c] = ok ? *reinterpret_cast<const uint4*>(Vb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c)
+        if (posof(0, c) == pos) {  // this launch's row, after the acquire
+          kr[c] = *reinterpret_cast<const uint4*>(Kb + (int64_t)pos * hd);
+          vr[c] = *reinterpret_cast<const uint4*>(Vb + (int64_t)pos * hd);
+        }
     }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      stats[2 * hh] = m;
-      stats[2 * hh + 1] = sum;
+    float sc[MAXC];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const uint4 k8 = kr[c];
+      float d = q[0] * bf16_lo(k8.x);
+      d = fmaf(q[1], bf16_hi(k8.x), d);
+      d = fmaf(q[2], bf16_lo(k8.y), d);
+      d = fmaf(q[3], bf16_hi(k8.y), d);
+      d = fmaf(q[4], bf16_lo(k8.z), d);
+      d = fmaf(q[5], bf16_hi(k8.z), d);
+      d = fmaf(q[6], bf16_lo(k8.w), d);
+      d = fmaf(q[7], bf16_hi(k8.w), d);
+      d = group_sum<LH>(d);
+      sc[c] = posof(blk, c) < p1 ? d : -INFINITY;
+      bm = fmaxf(bm, sc[c]);
     }
+    const float nm = fmaxf(M, bm);
+    const float alpha = M == -INFINITY ? 0.0f : __expf(M - nm);
+    Ls *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const float p = sc[c] == -INFINITY ? 0.0f : __expf(sc[c] - nm);
+      Ls += p;
+      const uint4 v8 = vr[c];
+      acc[0] = fmaf(p, bf16_lo(v8.x), acc[0]);
+      acc[1] = fmaf(p, bf16_hi(v8.x), acc[1]);
+      acc[2] = fmaf(p, bf16_lo(v8.y), acc[2]);
+      acc[3] = fmaf(p, bf16_hi(v8.y), acc[3]);
+      acc[4] = fmaf(p, bf16_lo(v8.z), acc[4]);
+      acc[5] = fmaf(p, bf16_hi(v8.z), acc[5]);
+      acc[6] = fmaf(p, bf16_lo(v8.w), acc[6]);
+      acc[7] = fmaf(p, bf16_hi(v8.w), acc[7]);
+    }
+    M = nm;
   }
+  // merge the (wave, position group) states of each head through LDS
+  float* wacc = smem + P.lds_att;         // [kWaves*64][8]
+  float* wst = wacc + kWaves * 64 * 8;    // [kWaves*64][2]
+  *reinterpret_cast<float4*>(wacc + tid * 8) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(wacc + tid * 8 + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  wst[tid * 2] = M;
+  wst[tid * 2 + 1] = Ls;
   __syncthreads();
-  // pass 3: sum_j p_j V_j
-  float acc[GRP][8];
+  for (int i = tid; i < nh * hd; i += kThreads) {
+    const int hq = i / hd, e = i - hq * hd, ci = e >> 3, ee = e & 7;
+    float mt = -INFINITY;
 #pragma unroll
-  for (int hh = 0; hh < GRP; ++hh)
+    for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
-  for (int jb = wave * PPW; jb < len; jb += kWaves * PPW) {
-    const int j = jb + sub;
-    const bool ok = j < len;
-    uint4 v8 = make_uint4(0, 0, 0, 0);
-    if (ok) v8 = *reinterpret_cast<const uint4*>(Vb + (int64_t)(p0 + j) * hd + li * 8);
-    const float vf[8] = {bf16_lo(v8.x), bf16_hi(v8.x), bf16_lo(v8.y), bf16_hi(v8.y),
-                         bf16_lo(v8.z), bf16_hi(v8.z), bf16_lo(v8.w), bf16_hi(v8.w)};
+      for (int q2 = 0; q2 < PW; ++q2) mt = fmaxf(mt, wst[(w * 64 + q2 * LH * GP + hq * LH) * 2]);
+    float o = 0.0f, lsum = 0.0f;
 #pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-      const float p = ok ? sc[hh * P.att_maxlen + j] : 0.0f;
+    for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < GRP; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[hh][e];
-      for (int o = LP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[hh][e] = v;
-    }
-  if (sub == 0) {
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ored[(wave * GRP + hh) * hd + li * 8 + e] = acc[hh][e];
-  }
-  __syncthreads();
-  for (int i = opaque_tid(); i < GRP * hd; i += kThreads) {
-    const int hh = i / hd, e = i - hh * hd;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += ored[(w * GRP + hh) * hd + e];
-    float* dst = P.part + (((int64_t)l * P.nq + h0 + hh) * S + s) * (hd + 2);
-    dst[e] = v;
+      for (int q2 = 0; q2 < PW; ++q2) {
+        const int ln = w * 64 + q2 * LH * GP + hq * LH;
+        const float mw = wst[ln * 2];
+        const float f = mw == -INFINITY ? 0.0f : __expf(mw - mt);
+        o = fmaf(f, wacc[(ln + ci) * 8 + ee], o);
+        lsum = fmaf(f, wst[ln * 2 + 1], lsum);
+      }
+    float* dst = P.part + (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2);
+    st_agent(dst + e, o);
     if (e == 0) {
-      dst[hd] = stats[2 * hh];
-      dst[hd + 1] = stats[2 * hh + 1];
+      st_agent(dst + hd, mt);
+      st_agent(dst + hd + 1, lsum);
     }
   }
   __syncthreads();
-  (void)red;
+  return true;
+}
+
+template <int LH, int GP>
+__device__ __forceinline__ bool attn_heads(const VmParams& P, const DevTask& t, int l, int g, int s, int S,
+                                           int p0, int p1, float* smem) {
+  const int grp = P.nq / P.nkv;
+  constexpr int MAXC = (64 / (LH * GP)) == 1 ? 8 : 4;
+  for (int h0 = 0; h0 < grp; h0 += GP)  // later passes find the counters reached
+    if (!attn_split<LH, GP, MAXC>(P, t, l, g, g * grp + h0, min(GP, grp - h0), s, S, p0, p1, smem))
+      return false;
+  return true;
 }
 
 __device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], g = t.p[1], s = t.p[2], S = t.p[3];
-  int* flag = reinterpret_cast<int*>(smem + kWaves);
-  if (!vm_wait(P, t, flag)) return false;
   const int n = P.pos + 1;
   const int p0 = (int)(((int64_t)s * n) / S), p1 = (int)(((int64_t)(s + 1) * n) / S);
   const int grp = P.nq / P.nkv, hd = P.hd;
   if (p1 <= p0) {
+    int* flag = reinterpret_cast<int*>(smem + kWaves);
+    if (!vm_wait(P, t, flag)) return false;
     for (int i = opaque_tid(); i < grp * (hd + 2); i += kThreads) {
       const int hh = i / (hd + 2), e = i - hh * (hd + 2);
       float* dst = P.part + (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2);
-      dst[e] = e == hd ? -INFINITY : 0.0f;
+      st_agent(dst + e, e == hd ? -INFINITY : 0.0f);
     }
   } else {
-    for (int h0 = 0; h0 < grp; h0 += 8) {
-      const int nh = min(8, grp - h0);
-      const int hb = g * grp + h0;
-      switch (nh) {
-        case 1: attn_block<1>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 2: attn_block<2>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 3: attn_block<3>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 4: attn_block<4>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 5: attn_block<5>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 6: attn_block<6>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        case 7: attn_block<7>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-        default: attn_block<8>(P, l, g, hb, s, S, p0, p1 - p0, smem); break;
-      }
+    // GP = heads per pass: the group size rounded up to a power of two,
+    // limited by the 64 lanes of a wave
+    const int gp = grp == 1 ? 1 : grp == 2 ? 2 : grp <= 4 ? 4 : 8;
+    bool ok;
+    if (hd == 64) {
+      ok = gp == 1 ? attn_heads<8, 1>(P, t, l, g, s, S, p0, p1, smem)
+         : gp == 2 ? attn_heads<8, 2>(P, t, l, g, s, S, p0, p1, smem)
+         : gp == 4 ? attn_heads<8, 4>(P, t, l, g, s, S, p0, p1, smem)
+                   : attn_heads<8, 8>(P, t, l, g, s, S, p0, p1, smem);
+    } else if (hd == 128) {
+      ok = gp == 1 ? attn_heads<16, 1>(P, t, l, g, s, S, p0, p1, smem)
+         : gp == 2 ? attn_heads<16, 2>(P, t, l, g, s, S, p0, p1, smem)
+                   : attn_heads<16, 4>(P, t, l, g, s, S, p0, p1, smem);
+    } else {
+      ok = gp == 1 ? attn_heads<32, 1>(P, t, l, g, s, S, p0, p1, smem)
+                   : attn_heads<32, 2>(P, t, l, g, s, S, p0, p1, smem);
     }
+    if (!ok) return false;
   }
   vm_signal(P, t);
   return true;
 }
 
+// Log-sum-exp merge of the S split partials of query head h in one round
+// trip: thread i loads float4 chunk (i % (hd/4)) of split (i / (hd/4)) and
+// that split's (max, sum); the scaled chunks are summed per output element
+// through LDS in split order.
 __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], h = t.p[1], S = t.p[2];
   int* flag = reinterpret_cast<int*>(smem + kWaves);
-  if (!vm_wait(P, t, flag)) return false;
-  const int hd = P.hd;
-  float* wts = smem + P.lds_att;  // S weights
   float* red = smem;
+  const int hd = P.hd, hq = hd >> 2, tid = opaque_tid();
+  if (!vm_wait(P, t, flag)) return false;
   const float* part = P.part + ((int64_t)l * P.nq + h) * S * (hd + 2);
+  float* wsum = smem + P.lds_att;  // [S][hd] scaled chunks
+  float* wts = wsum + S * hd;      // [S]
   // global max of the split maxima
   float m = -INFINITY;
-  for (int s = opaque_tid(); s < S; s += kThreads) m = fmaxf(m, part[(int64_t)s * (hd + 2) + hd]);
+  for (int sp = tid; sp < S; sp += kThreads) m = fmaxf(m, part[(int64_t)sp * (hd + 2) + hd]);
   m = wave_max(m);
-  if ((opaque_tid() & 63) == 0) red[opaque_tid() >> 6] = m;
-  __syncthreads();
-  float M = red[0];
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  // chunk loads issued before the barrier so they overlap the reduction
+  const int items = S * hq;
+  float4 ch[4];
+  int nit = 0;
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
+  for (int k = 0; k < 4; ++k) {
+    const int it = tid + k * kThreads;
+    if (it < items) {
+      const int sp = it / hq, qd = it - sp * hq;
+      ch[k] = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
+      nit = k + 1;
+    }
+  }
+  __syncthreads();
+  float Mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, red[w]);
   __syncthreads();
   float lsum = 0.0f;
-  for (int s = opaque_tid(); s < S; s += kThreads) {
-    const float ms = part[(int64_t)s * (hd + 2) + hd];
-    const float wgt = ms == -INFINITY ? 0.0f : expf(ms - M);
-    wts[s] = wgt;
-    lsum += wgt * part[(int64_t)s * (hd + 2) + hd + 1];
+  for (int sp = tid; sp < S; sp += kThreads) {
+    const float ms = part[(int64_t)sp * (hd + 2) + hd];
+    const float wgt = ms == -INFINITY ? 0.0f : __expf(ms - Mx);
+    wts[sp] = wgt;
+    lsum += wgt * part[(int64_t)sp * (hd + 2) + hd + 1];
   }
-  const float Ltot = block_sum(lsum, red);  // barrier also publishes wts
+  const float Ltot = block_sum(lsum, red);  // its barriers also publish wts
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < nit) {
+      const int it = tid + k * kThreads;
+      const int sp = it / hq, qd = it - sp * hq;
+      const float wgt = wts[sp];
+      *reinterpret_cast<float4*>(wsum + sp * hd + qd * 4) =
+          make_float4(wgt * ch[k].x, wgt * ch[k].y, wgt * ch[k].z, wgt * ch[k].w);
+    }
+  }
+  for (int it = tid + 4 * kThreads; it < items; it += kThreads) {  // S*hd/4 > 2048
+    const int sp = it / hq, qd = it - sp * hq;
+    const float4 c = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
+    const float wgt = wts[sp];
+    *reinterpret_cast<float4*>(wsum + sp * hd + qd * 4) = make_float4(wgt * c.x, wgt * c.y, wgt * c.z, wgt * c.w);
+  }
+  __syncthreads();
   const float inv = 1.0f / Ltot;
-  for (int e = opaque_tid(); e < hd; e += kThreads) {
+  for (int e = tid; e < hd; e += kThreads) {
     float v = 0.0f;
-    for (int s = 0; s < S; ++s) v = fmaf(wts[s], part[(int64_t)s * (hd + 2) + e], v);
-    P.o[(int64_t)l * P.nq * hd + (int64_t)h * hd + e] = v * inv;
+    for (int sp = 0; sp < S; ++sp) v += wsum[sp * hd + e];
+    st_agent(P.o + (int64_t)l * P.nq * hd + (int64_t)h * hd + e, v * inv);
   }
   vm_signal(P, t);
   return true;
@@ -932,6 +1083,29 @@ __global__ void __launch_bounds__(kThreads) amk_vm(VmParams P) {
     }
     if (!ok) return;
   }
+}
+
+// Plain streaming read of `bytes` (multiple of 16): grid-stride 16-byte
+// loads, 4 in flight per thread, one partial sum per block so the loads are
+// not dead.  Measures the read bandwidth the memory system sustains.
+__global__ void __launch_bounds__(256) amk_stream_read(const uint4* __restrict__ src, uint64_t n16,
+                                                        float* __restrict__ out) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i];
+    const uint4 b = src[i + stride];
+    const uint4 c = src[i + 2 * stride];
+    const uint4 d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  // data-dependent store keeps the loads alive
+  if (acc == 0x9E3779B9u) out[blockIdx.x] = 1.0f;
 }
 
 template __global__ void amk_vm<4>(VmParams);
@@ -975,6 +1149,8 @@ struct amk_engine {
   int64_t written = 0;  // positions 0..written-1 hold KV rows
   int64_t steps = 0;
   int wallclock_khz = 100000;
+  int32_t n_tasks = 0;
+  uint64_t* d_trace = nullptr;  // allocated on first amk_engine_set_trace(e, 1)
 };
 
 namespace amk {
@@ -1075,9 +1251,9 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   const int64_t res_floats = std::max({2 * max_rows((int64_t)(m.n_heads + 2 * m.n_kv_heads) * hd / 2, c.tiles_qkv),
                                        max_rows(H, c.tiles_o), 2 * max_rows(F, c.tiles_gateup),
                                        max_rows(H, c.tiles_down), max_rows(m.vocab, c.tiles_lm)});
-  const int64_t grp = m.n_heads / m.n_kv_heads, gb = std::min<int64_t>(grp, 8);
-  const int64_t maxlen = (m.max_ctx + c.attn_splits - 1) / c.attn_splits + 1;
-  const int64_t att_floats = std::max<int64_t>(gb * hd + gb * maxlen + 2 * gb + kWaves * gb * hd, c.attn_splits);
+  const int64_t grp = m.n_heads / m.n_kv_heads, gb = std::min<int64_t>(grp, 4);
+  const int64_t maxlen = 0;
+  const int64_t att_floats = std::max<int64_t>(kWaves * 64 * 10, (int64_t)c.attn_splits * (hd + 1));
   const int64_t head = 16;  // block-reduction slots + flag + int8 sum
   const int64_t lds_x = head, lds_res = lds_x + xs_floats;
   const int64_t lds_att = head;
@@ -1108,11 +1284,13 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   e->max_prod = 1;
   for (uint32_t p : P) e->max_prod = std::max(e->max_prod, p);
   e->n_counters = std::max(1, s->n_counters);
+  e->n_tasks = (int32_t)s->tasks.size();
   std::vector<DevTask> dt(s->tasks.size());
   for (size_t i = 0; i < s->tasks.size(); ++i) {
     const Task& t = s->tasks[i];
     DevTask d{};
     d.type = t.type;
+    d.id = (int32_t)i;
     d.nwait = (int32_t)t.waits.size();
     d.nsig = (int32_t)t.sigs.size();
     std::copy(t.p, t.p + 8, d.p);
@@ -1231,6 +1409,25 @@ amk_status amk_engine_set_kv_length(amk_engine* e, int32_t n) {
   return AMK_OK;
 }
 
+amk_status amk_engine_set_trace(amk_engine* e, int32_t enable) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  if (enable && !e->d_trace) {
+    amk_status st = dev_alloc(e, &e->d_trace, (size_t)std::max(1, e->n_tasks) * 4);
+    if (st != AMK_OK) return st;
+  }
+  e->params.trace = enable ? e->d_trace : nullptr;
+  return AMK_OK;
+}
+
+amk_status amk_engine_read_trace(amk_engine* e, uint64_t* out, int64_t n_values, int32_t* clock_khz) {
+  if (!e || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  if (!e->d_trace) return fail(AMK_ERR_INVALID_ARG, "tracing was never enabled");
+  if (n_values != (int64_t)e->n_tasks * 4) return fail(AMK_ERR_INVALID_ARG, "need 4 values per task");
+  HIP_TRY(hipMemcpy(out, e->d_trace, sizeof(uint64_t) * n_values, hipMemcpyDeviceToHost));
+  if (clock_khz) *clock_khz = e->wallclock_khz;
+  return AMK_OK;
+}
+
 amk_status amk_engine_set_spin_budget(amk_engine* e, int64_t us) {
   if (!e || us <= 0) return fail(AMK_ERR_INVALID_ARG, "bad engine or budget");
   e->params.spin_ticks = (uint64_t)us * (uint64_t)e->wallclock_khz / 1000u;
@@ -1240,6 +1437,14 @@ amk_status amk_engine_set_spin_budget(amk_engine* e, int64_t us) {
 amk_status amk_engine_steps(const amk_engine* e, int64_t* out) {
   if (!e || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
   *out = e->steps;
+  return AMK_OK;
+}
+
+amk_status amk_stream_read_probe(const void* src, size_t bytes, float* out, int32_t blocks, void* stream) {
+  if (!src || !out || blocks < 1 || bytes % 16) return fail(AMK_ERR_INVALID_ARG, "bad probe arguments");
+  hipLaunchKernelGGL(amk_stream_read, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), (uint64_t)(bytes / 16), out);
+  HIP_TRY(hipGetLastError());
   return AMK_OK;
 }
 

@@ -30,6 +30,27 @@ def test_tiny_full_protocol():
     assert np.allclose(g, o, rtol=2 ** -7, atol=1e-6)
 
 
+def test_1b_tied_short_and_long():
+    """~1B decoder with tied embeddings (head_dim 64, 4 query heads per kv
+    head): an 8-token prompt + 8 decode steps, then 3 decode steps after a
+    seeded 128-row KV prefix; every step compared."""
+    wl = synth.get("1b")
+    w = synth.model_weights(wl, seed=1)
+    toks = synth.tokens(2, 16, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks)
+    del eng
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"1b short: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+    P = wl.prompt_len
+    kvp = synth.kv_prefix(wl, P, seed=3)
+    toks = synth.tokens(2, P + 3, wl.vocab)[P:]
+    res, eng, _ = teacher_forced(wl, w, toks, kv_prefix=kvp, start=P)
+    del eng
+    _free()
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"1b long: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
 @pytest.fixture(scope="module")
 def w8b():
     wl = synth.get("8b")
