@@ -78,6 +78,14 @@ typedef struct {
   int32_t cu_policy;       /* 0: task i of T -> queue i*num_cus/T; 1: i % num_cus */
   int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16 */
   uint32_t fuse_flags;     /* AMK_FUSE_* bits; only AMK_FUSE_DEFAULT is built */
+  /* Queue-walk knobs (no effect on the DAG the safety gate checks):
+   * poll_mode 0: the polling wave issues its weight prologue before the
+   *   wait like the others; 1: after the wait (its poll is then not queued
+   *   behind its own loads).
+   * release_mode 0: all waves wait for their stores, barrier, then the
+   *   release; 1: the epilogue stores and the release are issued by the
+   *   polling wave alone while the others start the next task. */
+  int32_t poll_mode, release_mode;
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */

@@ -10,7 +10,7 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libamk.so")
+LIB_PATH = os.environ.get("AMK_LIB_PATH") or os.path.join(_HERE, "libamk.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -57,7 +57,8 @@ class ModelConfig(ctypes.Structure):
 class ScheduleConfig(ctypes.Structure):
     _fields_ = [(n, _i32) for n in ("num_cus", "wg_threads", "tiles_qkv", "tiles_o",
                                     "tiles_gateup", "tiles_down", "tiles_lm", "attn_splits",
-                                    "cu_policy", "pipeline_depth")] + [("fuse_flags", _u32)]
+                                    "cu_policy", "pipeline_depth")] + [("fuse_flags", _u32)] + [
+        (n, _i32) for n in ("poll_mode", "release_mode")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

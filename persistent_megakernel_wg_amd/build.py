@@ -42,7 +42,9 @@ def _compile(name, lang, extra):
     return obj, "\n".join(msgs)
 
 
-def build(extra_flags=(), verbose=False):
+def build(extra_flags=(), verbose=False, out=None):
+    """Compile and link; `out` defaults to the package's libamk.so."""
+    out = out or OUT
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra_flags)
     with concurrent.futures.ThreadPoolExecutor(max_workers=6) as ex:
@@ -53,13 +55,13 @@ def build(extra_flags=(), verbose=False):
             objs.append(obj)
             if verbose and msg:
                 print(f"[{futs[f]}]\n{msg}", file=sys.stderr)
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + sorted(objs)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -128,7 +128,8 @@ struct alignas(16) DevTask {
   uint32_t wthr[kMaxWaits];
   uint32_t wprod[kMaxWaits];  // producers of the counter (epoch stride)
   int32_t sctr[kMaxSigs];
-  int32_t pad1[4];
+  int32_t qslot;  // parity of the task's position in its queue (wait-flag slot)
+  int32_t pad1[3];
 };
 static_assert(sizeof(DevTask) == 128, "device task record is 128 bytes");
 

@@ -51,7 +51,7 @@ amk_status amk_default_schedule_config(const amk_model_config* model, int32_t de
   c.num_cus = device_cus;
   c.wg_threads = 512;
   c.cu_policy = 0;
-  c.pipeline_depth = 16;
+  c.pipeline_depth = 8;
   c.fuse_flags = AMK_FUSE_DEFAULT;
   return resolve_config(*model, c, out);
 }

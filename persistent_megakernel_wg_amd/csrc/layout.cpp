@@ -60,9 +60,12 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.attn_splits <= 0) c.attn_splits = std::max(1, c.num_cus / m.n_kv_heads);
   if (c.attn_splits > 256) return fail(AMK_ERR_UNSUPPORTED, "attn_splits must be at most 256");
   if (c.cu_policy != 0 && c.cu_policy != 1) return fail(AMK_ERR_UNSUPPORTED, "cu_policy must be 0 or 1");
-  if (c.pipeline_depth == 0) c.pipeline_depth = 16;
+  if (c.pipeline_depth == 0) c.pipeline_depth = 8;
   if (c.pipeline_depth != 4 && c.pipeline_depth != 8 && c.pipeline_depth != 16)
     return fail(AMK_ERR_UNSUPPORTED, "pipeline_depth must be 4, 8 or 16");
+  if (c.poll_mode != 0 && c.poll_mode != 1) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0 or 1");
+  if (c.release_mode != 0 && c.release_mode != 1)
+    return fail(AMK_ERR_UNSUPPORTED, "release_mode must be 0 or 1");
   if (c.fuse_flags == 0) c.fuse_flags = AMK_FUSE_DEFAULT;
   if (c.fuse_flags != AMK_FUSE_DEFAULT)
     return fail(AMK_ERR_UNSUPPORTED, "only the fully fused task set (AMK_FUSE_DEFAULT) is built");

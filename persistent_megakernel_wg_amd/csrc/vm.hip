@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <cstring>
 #include <vector>
 
@@ -58,8 +59,10 @@ struct VmParams {
   int32_t L, H, nq, nkv, hd, F, V, mc, S, wfmt, act_bf16;
   float eps;
   // LDS carve-up (float offsets into dynamic shared memory)
-  int32_t lds_x, lds_res, lds_att;
-  int32_t att_maxlen;
+  int32_t lds_x, lds_res, lds_att, res_floats;
+  // queue-walk knobs of the schedule configuration
+  int32_t poll_late;  // the polling wave issues its weight prologue after the wait
+  int32_t rel0;       // epilogue stores and release by wave 0 alone
 };
 
 // ------------------------------------------------------------- helpers --
@@ -174,8 +177,16 @@ __device__ __forceinline__ void st_agent(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer descriptor over [base, base + bytes).  Base and size are the same in
+// every lane; reading them through readfirstlane lets the compiler keep the
+// descriptor in scalar registers (a descriptor it must assume divergent
+// costs a loop over lanes around every buffer load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufFlags);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), (int)kBufFlags);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -189,8 +200,11 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // Thread 0 spins until every wait of the task holds, then performs the
 // agent-scope acquire; the workgroup barrier passes the result to all
 // threads.  Returns false when the spin budget ran out or another
-// workgroup already reported an error (the launch then drains).
-__device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int* flag) {
+// workgroup already reported an error (the launch then drains).  The flag
+// slot alternates with the task's queue position: waves that run ahead into
+// the next task cannot overwrite a flag a slower wave has yet to read.
+__device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int* flags) {
+  int* flag = flags + t.qslot;
   if (opaque_tid() == 0) {
     if (P.trace) P.trace[(size_t)t.id * 4 + 0] = wall_clock64();
     int ok = 1;
@@ -219,166 +233,166 @@ __device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int
   return *flag != 0;
 }
 
-// Release: every wave waits until its own stores have completed (all data
-// read by other workgroups is written with agent-scope stores, so completion
-// means visible at the device coherence point), the barrier joins the waves,
-// then thread 0 bumps each counter once with a relaxed agent-scope add.
+// Release.  Every store another workgroup reads is a write-through
+// agent-scope store, so its completion (vmcnt) means it is visible at the
+// device coherence point; lane 0 of wave 0 then bumps each counter with a
+// relaxed agent-scope add.  rel0 = 0: all waves wait for their stores and
+// meet at a barrier first.  rel0 = 1: only wave 0 issued such stores (the
+// epilogue ran on 64 threads), only it waits, and the other waves go on to
+// issue the next task's weight loads.
+__device__ __forceinline__ int epilogue_threads(const VmParams& P) { return P.rel0 ? 64 : kThreads; }
+
 __device__ __forceinline__ void vm_signal(const VmParams& P, const DevTask& t) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (opaque_tid() == 0) {
-    if (P.trace) P.trace[(size_t)t.id * 4 + 2] = wall_clock64();
-    for (int k = 0; k < t.nsig; ++k)
-      __hip_atomic_fetch_add(P.ctr + (size_t)t.sctr[k] * kCounterStride, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    if (P.trace) P.trace[(size_t)t.id * 4 + 3] = wall_clock64();
+  const int tid = opaque_tid();
+  if (!P.rel0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
-}
-
-// ------------------------------------------------------------- staging --
-// The activation vector of a GEMV is staged in LDS permuted so that lane l
-// of wave-load j reads its 8 values as two conflict-free float4 reads:
-// element e (chunk c = e/8, k = e%8, j = c/64, lane = c%64) lives at
-// ((j*2 + k/4)*64 + lane)*4 + k%4.  Padding up to whole wave-loads is zero.
-__device__ __forceinline__ int xperm(int e) {
-  const int c = e >> 3, k = e & 7;
-  return (((c >> 6) * 2 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
-}
-
-// x (fp32 or bf16 source) -> optional RMSNorm with bf16 gain -> optional bf16
-// rounding -> LDS.  n is a multiple of 8.
-template <bool SRC_BF16, bool NORM>
-__device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
-                        float* xs, float* red) {
-  const int n4 = n >> 2;
-  float ss = 0.0f;
-  for (int i = opaque_tid(); i < n4; i += kThreads) {
-    float4 v;
-    if (SRC_BF16) {
-      const uint2 b = reinterpret_cast<const uint2*>(src)[i];
-      v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
-    } else {
-      v = reinterpret_cast<const float4*>(src)[i];
-    }
-    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    if (!NORM && act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
-    *reinterpret_cast<float4*>(xs + xperm(i * 4)) = v;
-  }
-  // zero padding of the last wave-load
-  const int padded = ((n + 511) >> 9) << 9;
-  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
-    *reinterpret_cast<float4*>(xs + xperm(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (NORM) {
-    const float tot = block_sum(ss, red);  // contains barriers
-    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-    for (int i = opaque_tid(); i < n4; i += kThreads) {
-      float4* p = reinterpret_cast<float4*>(xs + xperm(i * 4));
-      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
-      float4 v = *p;
-      v.x = v.x * inv * bf16_lo(g.x);
-      v.y = v.y * inv * bf16_hi(g.x);
-      v.z = v.z * inv * bf16_lo(g.y);
-      v.w = v.w * inv * bf16_hi(g.y);
-      if (act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
-      *p = v;
+  if (tid < 64) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid == 0) {
+      if (P.trace) P.trace[(size_t)t.id * 4 + 2] = wall_clock64();
+      for (int k = 0; k < t.nsig; ++k)
+        __hip_atomic_fetch_add(P.ctr + (size_t)t.sctr[k] * kCounterStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      if (P.trace) P.trace[(size_t)t.id * 4 + 3] = wall_clock64();
     }
   }
-  __syncthreads();
 }
 
 // --------------------------------------------------------------- GEMV ---
-// bf16 rows.  `base` = first packed row of the task, `row_bytes` = K*2,
-// `nunits` units of RPU consecutive rows.  Wave w owns units w, w+8, ...
-// After the prologue issues the first DS steps (RPU loads each), `stage()`
-// runs the wait and the staging; results land in res[unit*RPU + r].
-template <int DS, int RPU, typename StageFn>
-__device__ __forceinline__ void gemv_bf16(const uint8_t* base, uint32_t row_bytes, int nunits, int K,
-                                          const float* xs, float* res, StageFn&& stage) {
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int nchunk = K >> 3;             // 16-byte chunks per row
-  const int J = (nchunk + 63) >> 6;      // wave-loads per row
-  const int jl = (nchunk - lane + 63) >> 6;  // wave-loads in which this lane has data
-  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
-  const __amdgpu_buffer_rsrc_t rs = rsrc(base, (uint32_t)nunits * RPU * row_bytes);
-  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
-
-  int ik = 0, ij = 0;
-  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
-  u32x4 buf[DS][RPU];
-  auto issue = [&](u32x4 (&b)[RPU]) {
-    const bool valid = ik < nk && ij < jl;
-#pragma unroll
-    for (int r = 0; r < RPU; ++r) b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
-    ioff += 1024u;
-    if (++ij == J) {
-      ij = 0;
-      ++ik;
-      ioff += unit_step;
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    issue(buf[s]);
-    __builtin_amdgcn_sched_barrier(0);
+// Streaming GEMV over `nunits` units of RPU consecutive packed rows (a RoPE or
+// gate/up pair when RPU = 2).  A step (unit, j) is one 16-byte load per lane
+// and row: 64 lanes cover a 1 KB-wide slab of the row, J slabs per row.  Work
+// split over the 8 waves:
+//   rounds: while 8 whole units remain, wave w owns unit w of the round, so
+//           the 8 waves stream 8 adjacent rows side by side (the workgroup's
+//           reads stay within a few DRAM pages);
+//   tail:   the R = nunits % 8 last units are cut into p = 8 / R (at most J)
+//           equal slab ranges each; wave w < R*p takes piece w % p of tail
+//           unit w / p.
+// So a wave's steps form its round units plus at most one tail segment, and
+// every segment lies inside one unit.  Each wave writes one partial per
+// segment to an LDS table; the finalize pass adds, per row, the partials of
+// the waves that covered its unit, in wave order (bit-reproducible).  Each
+// wave keeps DS steps of loads in flight in a register ring; the first DS are
+// issued before the task's wait (for wave 0, which polls, after it when
+// poll_late is set: a poll then does not queue behind its own weight loads).
+// Buffer loads whose offset lies past the task's rows return zero without
+// memory traffic.
+struct GemvSplit {
+  int J, nr, R, p, pl;  // slabs per row, rounds, tail units, pieces per tail unit, piece length
+  __device__ __forceinline__ GemvSplit(int nunits, int J_) : J(J_) {
+    nr = nunits / kWaves;
+    R = nunits - nr * kWaves;
+    p = R == 0 ? 0 : min(kWaves / R, J);
+    pl = p == 0 ? 0 : (J + p - 1) / p;
   }
-  stage();
-  const int total = nk * J;
-  const int iters = (total + DS - 1) / DS;
-  float acc[RPU];
-#pragma unroll
-  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
-  int cj = 0, ck = 0;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const float4 xa = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 0) * 64 + lane) * 4);
-      const float4 xb = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 1) * 64 + lane) * 4);
-#pragma unroll
-      for (int r = 0; r < RPU; ++r) {
-        const u32x4 w = buf[s][r];
-        float t = acc[r];
-        t = fmaf(bf16_lo(w.x), xa.x, t);
-        t = fmaf(bf16_hi(w.x), xa.y, t);
-        t = fmaf(bf16_lo(w.y), xa.z, t);
-        t = fmaf(bf16_hi(w.y), xa.w, t);
-        t = fmaf(bf16_lo(w.z), xb.x, t);
-        t = fmaf(bf16_hi(w.z), xb.y, t);
-        t = fmaf(bf16_lo(w.w), xb.z, t);
-        t = fmaf(bf16_hi(w.w), xb.w, t);
-        acc[r] = t;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      issue(buf[s]);
-      if (++cj == J) {
-        cj = 0;
-#pragma unroll
-        for (int r = 0; r < RPU; ++r) {
-          const float v = wave_sum(acc[r]);
-          if (lane == 0 && ck < nk) res[(wave + ck * kWaves) * RPU + r] = v;
-          acc[r] = 0.0f;
-        }
-        ++ck;
-      }
+  // tail segment of wave w: unit (index), first slab, length (0: none)
+  __device__ __forceinline__ void tail(int w, int* unit, int* j0, int* len) const {
+    *unit = 0;
+    *j0 = 0;
+    *len = 0;
+    if (w < R * p) {
+      const int q = w / p, k = w - q * p;
+      *unit = nr * kWaves + q;
+      *j0 = k * pl;
+      *len = max(0, min(J, *j0 + pl) - *j0);
     }
   }
-  __syncthreads();
+};
+
+// attention spreads positions over waves 1..7; wave 0 polls
+constexpr int kAttnWaves = kWaves - 1;
+
+// x for 16-byte chunks of E elements, staged so lane l of wave-load j reads
+// its E values as E/4 conflict-free float4s: element e (c = e/E, k = e%E,
+// j = c/64) at ((j*(E/4) + k/4)*64 + c%64)*4 + k%4.
+template <int E>
+__device__ __forceinline__ int xperm_e(int e) {
+  const int c = e / E, k = e % E;
+  return (((c >> 6) * (E / 4) + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
 }
 
-// int8 rows stored as q + 128 with one fp32 scale per row after the data:
-// row = s_r * (sum_k u_k x_k - 128 * sum_k x_k).  Chunks are 16 values; the
-// staged x uses 16-value chunks: element e (c = e/16, k = e%16, j = c/64) at
-// ((j*4 + k/4)*64 + c%64)*4 + k%4.
-__device__ __forceinline__ int xperm16(int e) {
-  const int c = e >> 4, k = e & 15;
-  return (((c >> 6) * 4 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
+__device__ __forceinline__ float f16_to_f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
-template <bool SRC_BF16, bool NORM>
-__device__ __forceinline__ void stage_x16(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
-                          float* xs, float* red, float* xsum) {
-  const int n4 = n >> 2;
+struct FmtBf16 {
+  static constexpr int E = 8;
+  static constexpr bool kMeta = false;
+  __device__ __forceinline__ static float dot(float t, u32x4 w, uint32_t, const float* xs, int cj, int lane,
+                                              const float*) {
+    const float4 xa = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 0) * 64 + lane) * 4);
+    const float4 xb = *reinterpret_cast<const float4*>(xs + ((cj * 2 + 1) * 64 + lane) * 4);
+    t = fmaf(bf16_lo(w.x), xa.x, t);
+    t = fmaf(bf16_hi(w.x), xa.y, t);
+    t = fmaf(bf16_lo(w.y), xa.z, t);
+    t = fmaf(bf16_hi(w.y), xa.w, t);
+    t = fmaf(bf16_lo(w.z), xb.x, t);
+    t = fmaf(bf16_hi(w.z), xb.y, t);
+    t = fmaf(bf16_lo(w.w), xb.z, t);
+    t = fmaf(bf16_hi(w.w), xb.w, t);
+    return t;
+  }
+};
+
+// int8 rows hold q + 128: row = s_r * (sum u x - 128 * sum x) (finalize)
+struct FmtInt8 {
+  static constexpr int E = 16;
+  static constexpr bool kMeta = false;
+  __device__ __forceinline__ static float dot(float t, u32x4 w, uint32_t, const float* xs, int cj, int lane,
+                                              const float*) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(xs + ((cj * 4 + q) * 64 + lane) * 4);
+      t = fmaf((float)((wd[q] >> 0) & 0xFFu), x.x, t);
+      t = fmaf((float)((wd[q] >> 8) & 0xFFu), x.y, t);
+      t = fmaf((float)((wd[q] >> 16) & 0xFFu), x.z, t);
+      t = fmaf((float)((wd[q] >> 24) & 0xFFu), x.w, t);
+    }
+    return t;
+  }
+};
+
+// int4 rows: a 16-byte chunk is 32 columns (a quarter group of 128) with the
+// group's {fp16 scale, fp16 zero}; word q holds columns 8q..8q+7, nibble j
+// column 2j and nibble j+4 column 2j+1.  Contribution s*(sum q x - z*sum x).
+struct FmtInt4 {
+  static constexpr int E = 32;
+  static constexpr bool kMeta = true;
+  __device__ __forceinline__ static float dot(float acc, u32x4 w, uint32_t m, const float* xs, int cj, int lane,
+                                              const float* csum) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    float d = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 xa = *reinterpret_cast<const float4*>(xs + ((cj * 8 + 2 * q) * 64 + lane) * 4);
+      const float4 xb = *reinterpret_cast<const float4*>(xs + ((cj * 8 + 2 * q + 1) * 64 + lane) * 4);
+      d = fmaf((float)((wd[q] >> 0) & 0xFu), xa.x, d);
+      d = fmaf((float)((wd[q] >> 16) & 0xFu), xa.y, d);
+      d = fmaf((float)((wd[q] >> 4) & 0xFu), xa.z, d);
+      d = fmaf((float)((wd[q] >> 20) & 0xFu), xa.w, d);
+      d = fmaf((float)((wd[q] >> 8) & 0xFu), xb.x, d);
+      d = fmaf((float)((wd[q] >> 24) & 0xFu), xb.y, d);
+      d = fmaf((float)((wd[q] >> 12) & 0xFu), xb.z, d);
+      d = fmaf((float)((wd[q] >> 28) & 0xFu), xb.w, d);
+    }
+    const float cs = csum[cj * 64 + lane];
+    return fmaf(f16_to_f(m & 0xFFFFu), d - f16_to_f(m >> 16) * cs, acc);
+  }
+};
+
+// x (fp32 or bf16 source) -> optional RMSNorm with bf16 gain -> optional bf16
+// rounding -> LDS in the chunk layout of format F; int8 also gets sum x,
+// int4 the per-chunk sums of x.  n is a multiple of 8.
+template <class F, bool SRC_BF16, bool NORM>
+__device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* gain, float eps,
+                                        int act_bf16, float* xs, float* red, float* xsum, float* csum) {
+  const int tid = opaque_tid(), n4 = n >> 2;
   float ss = 0.0f;
-  for (int i = opaque_tid(); i < n4; i += kThreads) {
+  for (int i = tid; i < n4; i += kThreads) {
     float4 v;
     if (SRC_BF16) {
       const uint2 b = reinterpret_cast<const uint2*>(src)[i];
@@ -387,17 +401,18 @@ __device__ __forceinline__ void stage_x16(const void* src, int n, const uint16_t
       v = reinterpret_cast<const float4*>(src)[i];
     }
     if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    *reinterpret_cast<float4*>(xs + xperm16(i * 4)) = v;
+    *reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4)) = v;
   }
-  const int padded = ((n + 1023) >> 10) << 10;
-  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
-    *reinterpret_cast<float4*>(xs + xperm16(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int slab = F::E * 64;  // elements per wave-load
+  const int padded = (n + slab - 1) / slab * slab;
+  for (int e = n + tid * 4; e < padded; e += kThreads * 4)
+    *reinterpret_cast<float4*>(xs + xperm_e<F::E>(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
   float inv = 1.0f;
   if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
   else __syncthreads();
   float sx = 0.0f;
-  for (int i = opaque_tid(); i < n4; i += kThreads) {
-    float4* p = reinterpret_cast<float4*>(xs + xperm16(i * 4));
+  for (int i = tid; i < n4; i += kThreads) {
+    float4* p = reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4));
     float4 v = *p;
     if (NORM) {
       const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
@@ -410,287 +425,169 @@ __device__ __forceinline__ void stage_x16(const void* src, int n, const uint16_t
     *p = v;
     sx += v.x + v.y + v.z + v.w;
   }
-  const float tot = block_sum(sx, red);
-  if (opaque_tid() == 0) *xsum = tot;
-  __syncthreads();
-}
-
-template <int DS, int RPU, typename StageFn>
-__device__ __forceinline__ void gemv_int8(const uint8_t* data, const float* scales, uint32_t row_bytes,
-                                          int nunits, int K, const float* xs, const float* xsum,
-                                          float* res, StageFn&& stage) {
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int nchunk = K >> 4;
-  const int J = (nchunk + 63) >> 6;
-  const int jl = (nchunk - lane + 63) >> 6;
-  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
-  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
-  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
-  int ik = 0, ij = 0;
-  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
-  u32x4 buf[DS][RPU];
-  auto issue = [&](u32x4 (&b)[RPU]) {
-    const bool valid = ik < nk && ij < jl;
-#pragma unroll
-    for (int r = 0; r < RPU; ++r) b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
-    ioff += 1024u;
-    if (++ij == J) {
-      ij = 0;
-      ++ik;
-      ioff += unit_step;
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    issue(buf[s]);
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (F::E == 16) {
+    const float tot = block_sum(sx, red);
+    if (tid == 0) *xsum = tot;
   }
-  stage();
-  const float sum_x = *xsum;
-  const int total = nk * J;
-  const int iters = (total + DS - 1) / DS;
-  float acc[RPU];
-#pragma unroll
-  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
-  int cj = 0, ck = 0;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      float4 xv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[q] = *reinterpret_cast<const float4*>(xs + ((cj * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-      for (int r = 0; r < RPU; ++r) {
-        const u32x4 w = buf[s][r];
-        float t = acc[r];
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          t = fmaf((float)((wd[q] >> 0) & 0xFFu), xv[q].x, t);
-          t = fmaf((float)((wd[q] >> 8) & 0xFFu), xv[q].y, t);
-          t = fmaf((float)((wd[q] >> 16) & 0xFFu), xv[q].z, t);
-          t = fmaf((float)((wd[q] >> 24) & 0xFFu), xv[q].w, t);
-        }
-        acc[r] = t;
+  __syncthreads();
+  if constexpr (F::E == 32) {
+    for (int c = tid; c < padded / 32; c += kThreads) {
+      float t = 0.0f;
+      for (int k = 0; k < 32; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(xs + xperm_e<32>(c * 32 + k));
+        t += v.x + v.y + v.z + v.w;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      issue(buf[s]);
-      if (++cj == J) {
-        cj = 0;
-#pragma unroll
-        for (int r = 0; r < RPU; ++r) {
-          const float v = wave_sum(acc[r]);
-          if (lane == 0 && ck < nk) {
-            const int row = (wave + ck * kWaves) * RPU + r;
-            res[row] = scales[row] * (v - 128.0f * sum_x);
-          }
-          acc[r] = 0.0f;
-        }
-        ++ck;
-      }
+      csum[c] = t;
     }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
-// int4 rows: per row K/2 bytes (nibbles permuted so that (w >> 4j) &
-// 0x000F000F gives columns 2j, 2j+1 of an 8-column word), then per row K/128
-// {fp16 scale, fp16 zero}.  A 16-byte chunk is 32 columns = a quarter group.
-// Staged x: 32-value chunks, element e (c = e/32, k = e%32, j = c/64) at
-// ((j*8 + k/4)*64 + c%64)*4 + k%4, plus per-chunk sums of x.
-__device__ __forceinline__ int xperm32(int e) {
-  const int c = e >> 5, k = e & 31;
-  return (((c >> 6) * 8 + (k >> 2)) * 64 + (c & 63)) * 4 + (k & 3);
-}
-
-template <bool SRC_BF16, bool NORM>
-__device__ __forceinline__ void stage_x32(const void* src, int n, const uint16_t* gain, float eps, int act_bf16,
-                          float* xs, float* red, float* csum) {
-  const int n4 = n >> 2;
-  float ss = 0.0f;
-  for (int i = opaque_tid(); i < n4; i += kThreads) {
-    float4 v;
-    if (SRC_BF16) {
-      const uint2 b = reinterpret_cast<const uint2*>(src)[i];
-      v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
-    } else {
-      v = reinterpret_cast<const float4*>(src)[i];
-    }
-    if (NORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    *reinterpret_cast<float4*>(xs + xperm32(i * 4)) = v;
-  }
-  const int padded = ((n + 2047) >> 11) << 11;
-  for (int e = n + opaque_tid() * 4; e < padded; e += kThreads * 4)
-    *reinterpret_cast<float4*>(xs + xperm32(e)) = make_float4(0.f, 0.f, 0.f, 0.f);
-  float inv = 1.0f;
-  if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
-  else __syncthreads();
-  for (int i = opaque_tid(); i < n4; i += kThreads) {
-    float4* p = reinterpret_cast<float4*>(xs + xperm32(i * 4));
-    float4 v = *p;
-    if (NORM) {
-      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
-      v.x = v.x * inv * bf16_lo(g.x);
-      v.y = v.y * inv * bf16_hi(g.x);
-      v.z = v.z * inv * bf16_lo(g.y);
-      v.w = v.w * inv * bf16_hi(g.y);
-    }
-    if (act_bf16) v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
-    *p = v;
-  }
-  __syncthreads();
-  // per-chunk sums of x (32 values each)
-  const int nch = padded >> 5;
-  for (int c = opaque_tid(); c < nch; c += kThreads) {
-    float s = 0.0f;
-    for (int k = 0; k < 32; k += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(xs + xperm32(c * 32 + k));
-      s += v.x + v.y + v.z + v.w;
-    }
-    csum[c] = s;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ float f16_to_f(uint32_t bits) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-}
-
-template <int DS, int RPU, typename StageFn>
-__device__ __forceinline__ void gemv_int4(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
-                                          uint32_t meta_row_bytes, int nunits, int K, const float* xs,
-                                          const float* csum, float* res, StageFn&& stage) {
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int nchunk = K >> 5;
+template <class F, int DS, int RPU, typename StageFn>
+__device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
+                                     uint32_t meta_row_bytes, int nunits, int K, const float* xs,
+                                     const float* csum, float* tbl, bool poll_late, StageFn&& stage) {
+  const int tid = opaque_tid(), lane = tid & 63;
+  const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nchunk = K / F::E;
   const int J = (nchunk + 63) >> 6;
-  const int jl = (nchunk - lane + 63) >> 6;
-  const int nk = wave < nunits ? (nunits - 1 - wave) / kWaves + 1 : 0;
+  const int jl = (nchunk - lane + 63) >> 6;  // slabs in which this lane has data
+  const GemvSplit sp(nunits, J);
+  int t_unit, t_j0, t_len;
+  sp.tail(sw, &t_unit, &t_j0, &t_len);
+  const int nA = sp.nr * J;   // steps in rounds
+  const int n = nA + t_len;   // steps of this wave
   const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
-  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, (uint32_t)nunits * RPU * meta_row_bytes);
-  const uint32_t unit_step = (uint32_t)kWaves * RPU * row_bytes - (uint32_t)J * 1024u;
-  const uint32_t unit_mstep = (uint32_t)kWaves * RPU * meta_row_bytes - (uint32_t)J * 64u;
-  int ik = 0, ij = 0;
-  uint32_t ioff = (uint32_t)wave * RPU * row_bytes + (uint32_t)lane * 16u;
-  // group of this lane's chunk: (j*64 + lane)/4 -> meta offset 4*group
-  uint32_t moff = (uint32_t)wave * RPU * meta_row_bytes + (uint32_t)(lane >> 2) * 4u;
+  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, F::kMeta ? (uint32_t)nunits * RPU * meta_row_bytes : 0u);
+  // issue state: steps issued, unit and slab of the next step
+  int ik = 0, iu = nA ? sw : t_unit, ij = nA ? 0 : t_j0;
   u32x4 buf[DS][RPU];
   uint32_t mbuf[DS][RPU];
-  auto issue = [&](u32x4 (&b)[RPU], uint32_t (&m)[RPU]) {
-    const bool valid = ik < nk && ij < jl;
+  auto issue = [&](u32x4 (&b)[RPU], uint32_t (&mb)[RPU]) {
+    const bool valid = ik < n && ij < jl;
+    const uint32_t off = (uint32_t)iu * RPU * row_bytes + (uint32_t)(ij * 64 + lane) * 16u;
+    const uint32_t moff = (uint32_t)iu * RPU * meta_row_bytes + (uint32_t)(ij * 16 + (lane >> 2)) * 4u;
 #pragma unroll
     for (int r = 0; r < RPU; ++r) {
-      b[r] = bload(rs, valid ? ioff + (uint32_t)r * row_bytes : kOob);
-      m[r] = __builtin_amdgcn_raw_buffer_load_b32(rm, valid ? moff + (uint32_t)r * meta_row_bytes : kOob, 0, 0);
+      b[r] = bload(rs, valid ? off + (uint32_t)r * row_bytes : kOob);
+      if constexpr (F::kMeta)
+        mb[r] = __builtin_amdgcn_raw_buffer_load_b32(rm, valid ? moff + (uint32_t)r * meta_row_bytes : kOob, 0, 0);
     }
-    ioff += 1024u;
-    moff += 64u;
+    ++ik;
     if (++ij == J) {
       ij = 0;
-      ++ik;
-      ioff += unit_step;
-      moff += unit_mstep;
+      iu += kWaves;
+    }
+    if (ik == nA) {
+      iu = t_unit;
+      ij = t_j0;
     }
   };
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    issue(buf[s], mbuf[s]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  stage();
-  const int total = nk * J;
-  const int iters = (total + DS - 1) / DS;
-  float acc[RPU];
-#pragma unroll
-  for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
-  int cj = 0, ck = 0;
-  for (int it = 0; it < iters; ++it) {
+  auto prologue = [&] {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      float4 xv[8];
+      issue(buf[s], mbuf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const bool late = poll_late && sw == 0;
+  if (!late) prologue();
+  stage();
+  if (late) prologue();
+  if (n > 0) {
+    const int iters = (n + DS - 1) / DS;
+    int ck = 0, cu = nA ? sw : t_unit, cj = nA ? 0 : t_j0;
+    float acc[RPU];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) xv[q] = *reinterpret_cast<const float4*>(xs + ((cj * 8 + q) * 64 + lane) * 4);
-      const float cs = csum[cj * 64 + lane];
+    for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int r = 0; r < RPU; ++r) {
-        const u32x4 w = buf[s][r];
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-        float d = 0.0f;
+      for (int s = 0; s < DS; ++s) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // word q holds columns 8q..8q+7 of the chunk; nibble j -> column 2j,
-          // nibble j+4 -> column 2j+1
+        for (int r = 0; r < RPU; ++r) acc[r] = F::dot(acc[r], buf[s][r], mbuf[s][r], xs, cj, lane, csum);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf[s], mbuf[s]);
+        ++ck;
+        const bool unit_end = ++cj == J;
+        if (ck <= n && (unit_end || ck == n)) {  // this wave's segment of unit cu is complete
 #pragma unroll
-          for (int jn = 0; jn < 4; ++jn) {
-            const float lo = (float)((wd[q] >> (4 * jn)) & 0xFu);
-            const float hi = (float)((wd[q] >> (4 * jn + 16)) & 0xFu);
-            const float4 xx = xv[q * 2 + (jn >> 1)];
-            const float x0 = (jn & 1) ? xx.z : xx.x;
-            const float x1 = (jn & 1) ? xx.w : xx.y;
-            d = fmaf(lo, x0, d);
-            d = fmaf(hi, x1, d);
+          for (int r = 0; r < RPU; ++r) {
+            const float v = wave_sum(acc[r]);
+            if (lane == 0) tbl[(cu * RPU + r) * kWaves + sw] = v;
+            acc[r] = 0.0f;
           }
         }
-        const uint32_t m = mbuf[s][r];
-        acc[r] = fmaf(f16_to_f(m & 0xFFFFu), d - f16_to_f(m >> 16) * cs, acc[r]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      issue(buf[s], mbuf[s]);
-      if (++cj == J) {
-        cj = 0;
-#pragma unroll
-        for (int r = 0; r < RPU; ++r) {
-          const float v = wave_sum(acc[r]);
-          if (lane == 0 && ck < nk) res[(wave + ck * kWaves) * RPU + r] = v;
-          acc[r] = 0.0f;
+        if (unit_end) {
+          cj = 0;
+          cu += kWaves;
         }
-        ++ck;
+        if (ck == nA) {
+          cu = t_unit;
+          cj = t_j0;
+        }
       }
     }
   }
   __syncthreads();
+}
+
+// sum of the partials of output row i (unit u = i / RPU): its owner in the
+// rounds, or the waves whose tail piece lies in unit u, in wave order
+template <int RPU>
+__device__ __forceinline__ float gemv_row(const float* tbl, int i, int nunits, int J) {
+  const int u = i / RPU;
+  const GemvSplit sp(nunits, J);
+  if (u < sp.nr * kWaves) return tbl[i * kWaves + u % kWaves];
+  const int q = u - sp.nr * kWaves;
+  float v = 0.0f;
+  for (int k = 0; k < sp.p; ++k)
+    if (k * sp.pl < J) v += tbl[i * kWaves + q * sp.p + k];
+  return v;
 }
 
 // Runs the projection rows [row0, row0 + nunits*RPU) of packed tensor `ptr`
-// in the model's weight format.  stage_src/norm describe the input vector.
-template <int DEPTH, int RPU, bool SRC_BF16, bool NORM>
+// (rows_total rows of K inputs) on the input vector `src` (RMSNorm'd with
+// `gain` when NORM), waiting for the task's counters after the first weight
+// loads are issued.  Results: res[i] for i < nunits*RPU (LDS).
+template <int DEPTH, int WFMT, int RPU, bool SRC_BF16, bool NORM>
 __device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, float* smem, const uint8_t* ptr,
-                        int64_t rows_total, int K, int row0, int nunits, const void* src,
-                        const uint16_t* gain) {
-  float* red = smem;               // kWaves floats
-  int* flag = reinterpret_cast<int*>(smem + kWaves);
-  float* scal = smem + kWaves + 1;  // one float (int8 sum of x)
+                                        int64_t rows_total, int K, int row0, int nunits, const void* src,
+                                        const uint16_t* gain) {
+  using F = typename std::conditional<WFMT == AMK_W_BF16, FmtBf16,
+            typename std::conditional<WFMT == AMK_W_INT8_ROW, FmtInt8, FmtInt4>::type>::type;
+  float* red = smem;                                  // kWaves floats
+  int* flag = reinterpret_cast<int*>(smem + kWaves);  // two wait-flag slots
+  float* xsum = smem + kWaves + 2;                    // sum of x (int8)
   float* xs = smem + P.lds_x;
   float* res = smem + P.lds_res;
+  float* tbl = res + P.res_floats;
+  const int padded = (K + F::E * 64 - 1) / (F::E * 64) * (F::E * 64);
+  float* csum = xs + padded;  // int4: per-chunk sums of x
+  const uint32_t rb = WFMT == AMK_W_BF16 ? (uint32_t)K * 2u : (WFMT == AMK_W_INT8_ROW ? (uint32_t)K : (uint32_t)K / 2u);
+  const uint32_t mb = WFMT == AMK_W_INT4_G128 ? (uint32_t)(K / 128) * 4u : (WFMT == AMK_W_INT8_ROW ? 4u : 0u);
+  const uint8_t* meta = ptr + rows_total * (int64_t)rb + (int64_t)row0 * mb;
   bool ok = true;
   constexpr int DS = DEPTH / RPU;
-  if (P.wfmt == AMK_W_BF16) {
-    const uint32_t rb = (uint32_t)K * 2u;
-    gemv_bf16<DS, RPU>(ptr + (int64_t)row0 * rb, rb, nunits, K, xs, res, [&] {
-      ok = vm_wait(P, t, flag);
-      if (ok) stage_x<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red);
-    });
-  } else if (P.wfmt == AMK_W_INT8_ROW) {
-    const uint32_t rb = (uint32_t)K;
-    const float* scales = reinterpret_cast<const float*>(ptr + rows_total * (int64_t)K) + row0;
-    gemv_int8<DS, RPU>(ptr + (int64_t)row0 * rb, scales, rb, nunits, K, xs, scal, res, [&] {
-      ok = vm_wait(P, t, flag);
-      if (ok) stage_x16<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, scal);
-    });
-  } else {
-    const uint32_t rb = (uint32_t)K / 2u, mb = (uint32_t)(K / 128) * 4u;
-    const uint8_t* meta = ptr + rows_total * (int64_t)rb + (int64_t)row0 * mb;
-    float* csum = xs + (((K + 2047) >> 11) << 11);
-    gemv_int4<DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, res, [&] {
-      ok = vm_wait(P, t, flag);
-      if (ok) stage_x32<SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, csum);
-    });
+  gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late != 0, [&] {
+    ok = vm_wait(P, t, flag);
+    if (ok) stage_x<F, SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, xsum, csum);
+  });
+  if (!ok) return false;
+  const int J = (K / F::E + 63) >> 6;
+  const int nrows = nunits * RPU, tid = opaque_tid();
+  for (int i = tid; i < nrows; i += kThreads) {
+    float v = gemv_row<RPU>(tbl, i, nunits, J);
+    if constexpr (WFMT == AMK_W_INT8_ROW)
+      v = reinterpret_cast<const float*>(meta)[i] * (v - 128.0f * *xsum);
+    res[i] = v;
   }
-  return ok;
+  __syncthreads();
+  return true;
 }
 
 // ---------------------------------------------------------------- tasks --
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], u0 = t.p[1], u1 = t.p[2];
   const int H = P.H, hd = P.hd, half = hd >> 1, nq = P.nq, nkv = P.nkv;
@@ -700,14 +597,17 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, fl
   bool ok;
   if (l == 0) {
     const void* src = P.wptr[0] + (int64_t)P.token * H * 2;
-    ok = project<DEPTH, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+    ok = project<DEPTH, WFMT, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
   } else {
     const void* src = P.x + ((int64_t)(l - 1) * 2 + 1) * H;
-    ok = project<DEPTH, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+    ok = project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
   }
   if (!ok) return false;
   const float* res = smem + P.lds_res;
-  for (int k = opaque_tid(); k < u1 - u0; k += kThreads) {
+  const int tid = opaque_tid();
+  const int EW = epilogue_threads(P);
+  if (tid < EW)
+  for (int k = tid; k < u1 - u0; k += EW) {
     const int u = u0 + k, hs = u / half, i = u - hs * half;
     float a = res[2 * k], b = res[2 * k + 1];
     if (hs < nq + nkv) {
@@ -731,16 +631,19 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, fl
   return true;
 }
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
   const int H = P.H, qd = P.nq * P.hd;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
   const float* src = P.o + (int64_t)l * qd;
-  if (!project<DEPTH, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)) return false;
+  if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)) return false;
   const float* res = smem + P.lds_res;
   float* dst = P.x + (int64_t)l * 2 * H;
-  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) {
+  const int tid = opaque_tid();
+  const int EW = epilogue_threads(P);
+  if (tid < EW)
+  for (int k = tid; k < r1 - r0; k += EW) {
     const int r = r0 + k;
     float resid;
     if (l == 0) resid = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
@@ -751,18 +654,21 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, 
   return true;
 }
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], j0 = t.p[1], j1 = t.p[2];
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_GATEUP];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_MLP_NORM]);
   const float* src = P.x + (int64_t)l * 2 * H;
-  if (!project<DEPTH, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, gain))
+  if (!project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, gain))
     return false;
   const float* res = smem + P.lds_res;
   float* dst = P.a + (int64_t)l * F;
-  for (int k = opaque_tid(); k < j1 - j0; k += kThreads) {
+  const int tid = opaque_tid();
+  const int EW = epilogue_threads(P);
+  if (tid < EW)
+  for (int k = tid; k < j1 - j0; k += EW) {
     const float g = res[2 * k], u = res[2 * k + 1];
     st_agent(dst + j0 + k, g / (1.0f + expf(-g)) * u);
   }
@@ -770,29 +676,32 @@ __device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t,
   return true;
 }
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool task_down(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
   const float* src = P.a + (int64_t)l * F;
-  if (!project<DEPTH, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)) return false;
+  if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)) return false;
   const float* res = smem + P.lds_res;
   const float* mid = P.x + (int64_t)l * 2 * H;
   float* dst = P.x + ((int64_t)l * 2 + 1) * H;
-  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) st_agent(dst + r0 + k, mid[r0 + k] + res[k]);
+  const int tid = opaque_tid();
+  const int EW = epilogue_threads(P);
+  if (tid < EW)
+    for (int k = tid; k < r1 - r0; k += EW) st_agent(dst + r0 + k, mid[r0 + k] + res[k]);
   vm_signal(P, t);
   return true;
 }
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool task_lmhead(const VmParams& P, const DevTask& t, float* smem) {
   const int r0 = t.p[0], r1 = t.p[1];
   const int H = P.H;
   const uint8_t* w = P.wptr[2];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
   const float* src = P.x + ((int64_t)(P.L - 1) * 2 + 1) * H;
-  if (!project<DEPTH, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)) return false;
+  if (!project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)) return false;
   const float* res = smem + P.lds_res;
   for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
   vm_signal(P, t);
@@ -818,16 +727,27 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
   const int hd = P.hd, pos = P.pos, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int pw = lane / (LH * GP), hh = (lane / LH) % GP, li = lane % LH;
   int* flag = reinterpret_cast<int*>(smem + kWaves);
-  const uint16_t* Kb = P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd + li * 8;
-  const uint16_t* Vb = P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd + li * 8;
-  auto posof = [&](int blk, int c) { return p0 + ((blk * MAXC + c) * kWaves + wave) * PW + pw; };
-  uint4 kr[MAXC], vr[MAXC];
+  // K / V rows of (l, g) through buffer descriptors: 32-bit offsets, and
+  // positions past p1 read as zero without touching memory
+  const uint32_t rows_bytes = (uint32_t)P.mc * hd * 2;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd, rows_bytes);
+  const uint32_t lane_off = (uint32_t)li * 16u, row_b = (uint32_t)hd * 2u;
+  // waves 1..7 take the positions; wave 0 polls and keeps no loads in flight
+  const int wsc = __builtin_amdgcn_readfirstlane(wave);
+  auto posof = [&](int blk, int c) {
+    return p0 + ((blk * MAXC + c) * kAttnWaves + (wsc - 1)) * PW + pw;
+  };
+  auto koff = [&](int j, bool ok) { return ok ? (uint32_t)j * row_b + lane_off : kOob; };
+  u32x4 kr[MAXC], vr[MAXC];
+  if (wsc != 0) {
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int j = posof(0, c);
-    const bool ok = j < p1 && j < pos;
-    kr[c] = ok ? *reinterpret_cast<const uint4*>(Kb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
-    vr[c] = ok ? *reinterpret_cast<const uint4*>(Vb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = posof(0, c);
+      const uint32_t o = koff(j, j < p1 && j < pos);
+      kr[c] = bload(rk, o);
+      vr[c] = bload(rv, o);
+    }
   }
   if (!vm_wait(P, t, flag)) return false;
   const bool hv = hh < nh;
@@ -844,30 +764,30 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   const int len = p1 - p0;
-  const int per_blk = MAXC * kWaves * PW;
-  const int nblk = (len + per_blk - 1) / per_blk;
+  const int per_blk = MAXC * kAttnWaves * PW;
+  const int nblk = wsc == 0 ? 0 : (len + per_blk - 1) / per_blk;
   for (int blk = 0; blk < nblk; ++blk) {
     if (blk > 0) {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int j = posof(blk, c);
-        const bool ok = j < p1;
-        kr[c] = ok ? *reinterpret_cast<const uint4*>(Kb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
-        vr[c] = ok ? *reinterpret_cast<const uint4*>(Vb + (int64_t)j * hd) : make_uint4(0, 0, 0, 0);
+        const uint32_t o = koff(j, j < p1);
+        kr[c] = bload(rk, o);
+        vr[c] = bload(rv, o);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < MAXC; ++c)
         if (posof(0, c) == pos) {  // this launch's row, after the acquire
-          kr[c] = *reinterpret_cast<const uint4*>(Kb + (int64_t)pos * hd);
-          vr[c] = *reinterpret_cast<const uint4*>(Vb + (int64_t)pos * hd);
+          kr[c] = bload(rk, koff(pos, true));
+          vr[c] = bload(rv, koff(pos, true));
         }
     }
     float sc[MAXC];
     float bm = -INFINITY;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const uint4 k8 = kr[c];
+      const u32x4 k8 = kr[c];
       float d = q[0] * bf16_lo(k8.x);
       d = fmaf(q[1], bf16_hi(k8.x), d);
       d = fmaf(q[2], bf16_lo(k8.y), d);
@@ -889,7 +809,7 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
     for (int c = 0; c < MAXC; ++c) {
       const float p = sc[c] == -INFINITY ? 0.0f : __expf(sc[c] - nm);
       Ls += p;
-      const uint4 v8 = vr[c];
+      const u32x4 v8 = vr[c];
       acc[0] = fmaf(p, bf16_lo(v8.x), acc[0]);
       acc[1] = fmaf(p, bf16_hi(v8.x), acc[1]);
       acc[2] = fmaf(p, bf16_lo(v8.y), acc[2]);
@@ -909,6 +829,7 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
   wst[tid * 2] = M;
   wst[tid * 2 + 1] = Ls;
   __syncthreads();
+  float* wout = wst + kWaves * 64 * 2;  // [nh][hd] outputs, then [nh][2] stats
   for (int i = tid; i < nh * hd; i += kThreads) {
     const int hq = i / hd, e = i - hq * hd, ci = e >> 3, ee = e & 7;
     float mt = -INFINITY;
@@ -927,14 +848,21 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
         o = fmaf(f, wacc[(ln + ci) * 8 + ee], o);
         lsum = fmaf(f, wst[ln * 2 + 1], lsum);
       }
-    float* dst = P.part + (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2);
-    st_agent(dst + e, o);
+    wout[i] = o;
     if (e == 0) {
-      st_agent(dst + hd, mt);
-      st_agent(dst + hd + 1, lsum);
+      wout[nh * hd + hq * 2] = mt;
+      wout[nh * hd + hq * 2 + 1] = lsum;
     }
   }
   __syncthreads();
+  const int EW = epilogue_threads(P);
+  if (tid < EW) {  // the releasing threads store everything other workgroups read
+    for (int i = tid; i < nh * (hd + 2); i += EW) {
+      const int hq = i / (hd + 2), e = i - hq * (hd + 2);
+      const float v = e < hd ? wout[hq * hd + e] : wout[nh * hd + hq * 2 + (e - hd)];
+      st_agent(P.part + (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2) + e, v);
+    }
+  }
   return true;
 }
 
@@ -942,10 +870,12 @@ template <int LH, int GP>
 __device__ __forceinline__ bool attn_heads(const VmParams& P, const DevTask& t, int l, int g, int s, int S,
                                            int p0, int p1, float* smem) {
   const int grp = P.nq / P.nkv;
-  constexpr int MAXC = (64 / (LH * GP)) == 1 ? 8 : 4;
-  for (int h0 = 0; h0 < grp; h0 += GP)  // later passes find the counters reached
+  constexpr int MAXC = 4;
+  for (int h0 = 0; h0 < grp; h0 += GP) {  // later passes find the counters reached
+    if (h0 > 0) __syncthreads();
     if (!attn_split<LH, GP, MAXC>(P, t, l, g, g * grp + h0, min(GP, grp - h0), s, S, p0, p1, smem))
       return false;
+  }
   return true;
 }
 
@@ -957,11 +887,14 @@ __device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, f
   if (p1 <= p0) {
     int* flag = reinterpret_cast<int*>(smem + kWaves);
     if (!vm_wait(P, t, flag)) return false;
-    for (int i = opaque_tid(); i < grp * (hd + 2); i += kThreads) {
-      const int hh = i / (hd + 2), e = i - hh * (hd + 2);
-      float* dst = P.part + (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2);
-      st_agent(dst + e, e == hd ? -INFINITY : 0.0f);
-    }
+    const int tid = opaque_tid();
+    const int EW = epilogue_threads(P);
+    if (tid < EW)
+      for (int i = tid; i < grp * (hd + 2); i += EW) {
+        const int hh = i / (hd + 2), e = i - hh * (hd + 2);
+        float* dst = P.part + (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2);
+        st_agent(dst + e, e == hd ? -INFINITY : 0.0f);
+      }
   } else {
     // GP = heads per pass: the group size rounded up to a power of two,
     // limited by the 64 lanes of a wave
@@ -986,10 +919,10 @@ __device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, f
   return true;
 }
 
-// Log-sum-exp merge of the S split partials of query head h in one round
-// trip: thread i loads float4 chunk (i % (hd/4)) of split (i / (hd/4)) and
-// that split's (max, sum); the scaled chunks are summed per output element
-// through LDS in split order.
+// Log-sum-exp merge of the S split partials of query head h: one round trip
+// of loads (every thread its float4 chunks and, for threads below S, that
+// split's (max, sum)), then LDS: weights w_s = exp(m_s - M), scaled chunks
+// summed per output element in split order, o = sum / sum_s w_s l_s.
 __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, float* smem) {
   const int l = t.p[0], h = t.p[1], S = t.p[2];
   int* flag = reinterpret_cast<int*>(smem + kWaves);
@@ -999,31 +932,34 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, 
   const float* part = P.part + ((int64_t)l * P.nq + h) * S * (hd + 2);
   float* wsum = smem + P.lds_att;  // [S][hd] scaled chunks
   float* wts = wsum + S * hd;      // [S]
-  // global max of the split maxima
-  float m = -INFINITY;
-  for (int sp = tid; sp < S; sp += kThreads) m = fmaxf(m, part[(int64_t)sp * (hd + 2) + hd]);
-  m = wave_max(m);
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  // chunk loads issued before the barrier so they overlap the reduction
+  float2 ml = make_float2(-INFINITY, 0.0f);
+  if (tid < S) ml = *reinterpret_cast<const float2*>(part + (int64_t)tid * (hd + 2) + hd);
   const int items = S * hq;
   float4 ch[4];
-  int nit = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int it = tid + k * kThreads;
     if (it < items) {
       const int sp = it / hq, qd = it - sp * hq;
       ch[k] = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
-      nit = k + 1;
     }
   }
+  float m = ml.x;
+  for (int sp = tid + kThreads; sp < S; sp += kThreads) m = fmaxf(m, part[(int64_t)sp * (hd + 2) + hd]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   float Mx = red[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, red[w]);
   __syncthreads();
   float lsum = 0.0f;
-  for (int sp = tid; sp < S; sp += kThreads) {
+  if (tid < S) {
+    const float wgt = ml.x == -INFINITY ? 0.0f : __expf(ml.x - Mx);
+    wts[tid] = wgt;
+    lsum = wgt * ml.y;
+  }
+  for (int sp = tid + kThreads; sp < S; sp += kThreads) {
     const float ms = part[(int64_t)sp * (hd + 2) + hd];
     const float wgt = ms == -INFINITY ? 0.0f : __expf(ms - Mx);
     wts[sp] = wgt;
@@ -1032,15 +968,15 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, 
   const float Ltot = block_sum(lsum, red);  // its barriers also publish wts
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (k < nit) {
-      const int it = tid + k * kThreads;
+    const int it = tid + k * kThreads;
+    if (it < items) {
       const int sp = it / hq, qd = it - sp * hq;
       const float wgt = wts[sp];
       *reinterpret_cast<float4*>(wsum + sp * hd + qd * 4) =
           make_float4(wgt * ch[k].x, wgt * ch[k].y, wgt * ch[k].z, wgt * ch[k].w);
     }
   }
-  for (int it = tid + 4 * kThreads; it < items; it += kThreads) {  // S*hd/4 > 2048
+  for (int it = tid + 4 * kThreads; it < items; it += kThreads) {
     const int sp = it / hq, qd = it - sp * hq;
     const float4 c = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
     const float wgt = wts[sp];
@@ -1048,11 +984,13 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, 
   }
   __syncthreads();
   const float inv = 1.0f / Ltot;
-  for (int e = tid; e < hd; e += kThreads) {
-    float v = 0.0f;
-    for (int sp = 0; sp < S; ++sp) v += wsum[sp * hd + e];
-    st_agent(P.o + (int64_t)l * P.nq * hd + (int64_t)h * hd + e, v * inv);
-  }
+  const int EW = epilogue_threads(P);
+  if (tid < EW)
+    for (int e = tid; e < hd; e += EW) {
+      float v = 0.0f;
+      for (int sp = 0; sp < S; ++sp) v += wsum[sp * hd + e];
+      st_agent(P.o + (int64_t)l * P.nq * hd + (int64_t)h * hd + e, v * inv);
+    }
   vm_signal(P, t);
   return true;
 }
@@ -1064,25 +1002,29 @@ __device__ __forceinline__ bool task_nop(const VmParams& P, const DevTask& t, fl
   return true;
 }
 
-template <int DEPTH>
+template <int DEPTH, int WFMT>
+__device__ __forceinline__ bool run_one(const VmParams& P, const DevTask& t, float* smem) {
+  switch (t.type) {
+    case AMK_TASK_QKV: return task_qkv<DEPTH, WFMT>(P, t, smem);
+    case AMK_TASK_ATTN: return task_attn(P, t, smem);
+    case AMK_TASK_MERGE: return task_merge(P, t, smem);
+    case AMK_TASK_OPROJ: return task_oproj<DEPTH, WFMT>(P, t, smem);
+    case AMK_TASK_GATEUP: return task_gateup<DEPTH, WFMT>(P, t, smem);
+    case AMK_TASK_DOWN: return task_down<DEPTH, WFMT>(P, t, smem);
+    case AMK_TASK_LMHEAD: return task_lmhead<DEPTH, WFMT>(P, t, smem);
+    default: return task_nop(P, t, smem);
+  }
+}
+
+// Workgroup b walks queue b in order.  A task that fails its wait (spin
+// budget spent, or another workgroup reported an error) ends the walk; the
+// error word tells every other workgroup to stop at its next wait.
+template <int DEPTH, int WFMT>
 __global__ void __launch_bounds__(kThreads) amk_vm(VmParams P) {
   extern __shared__ __align__(16) float smem[];
   const int q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
-  for (int qi = q0; qi < q1; ++qi) {
-    const DevTask& t = P.tasks[P.queue[qi]];
-    bool ok;
-    switch (t.type) {
-      case AMK_TASK_QKV: ok = task_qkv<DEPTH>(P, t, smem); break;
-      case AMK_TASK_ATTN: ok = task_attn(P, t, smem); break;
-      case AMK_TASK_MERGE: ok = task_merge(P, t, smem); break;
-      case AMK_TASK_OPROJ: ok = task_oproj<DEPTH>(P, t, smem); break;
-      case AMK_TASK_GATEUP: ok = task_gateup<DEPTH>(P, t, smem); break;
-      case AMK_TASK_DOWN: ok = task_down<DEPTH>(P, t, smem); break;
-      case AMK_TASK_LMHEAD: ok = task_lmhead<DEPTH>(P, t, smem); break;
-      default: ok = task_nop(P, t, smem); break;
-    }
-    if (!ok) return;
-  }
+  for (int qi = q0; qi < q1; ++qi)
+    if (!run_one<DEPTH, WFMT>(P, P.tasks[P.queue[qi]], smem)) return;
 }
 
 // Plain streaming read of `bytes` (multiple of 16): grid-stride 16-byte
@@ -1108,9 +1050,15 @@ __global__ void __launch_bounds__(256) amk_stream_read(const uint4* __restrict__
   if (acc == 0x9E3779B9u) out[blockIdx.x] = 1.0f;
 }
 
-template __global__ void amk_vm<4>(VmParams);
-template __global__ void amk_vm<8>(VmParams);
-template __global__ void amk_vm<16>(VmParams);
+template __global__ void amk_vm<4, AMK_W_BF16>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT8_ROW>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT4_G128>(VmParams);
+template __global__ void amk_vm<8, AMK_W_BF16>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT8_ROW>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT4_G128>(VmParams);
+template __global__ void amk_vm<16, AMK_W_BF16>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT8_ROW>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT4_G128>(VmParams);
 
 }  // namespace amk
 
@@ -1124,11 +1072,20 @@ namespace {
     if (e_ != hipSuccess) return fail(AMK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
-const void* kernel_for_depth(int depth) {
+template <int D>
+const void* kernel_for_format(int wfmt) {
+  switch (wfmt) {
+    case AMK_W_INT8_ROW: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT8_ROW>);
+    case AMK_W_INT4_G128: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT4_G128>);
+    default: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_BF16>);
+  }
+}
+
+const void* kernel_for(int depth, int wfmt) {
   switch (depth) {
-    case 4: return reinterpret_cast<const void*>(&amk_vm<4>);
-    case 8: return reinterpret_cast<const void*>(&amk_vm<8>);
-    default: return reinterpret_cast<const void*>(&amk_vm<16>);
+    case 4: return kernel_for_format<4>(wfmt);
+    case 8: return kernel_for_format<8>(wfmt);
+    default: return kernel_for_format<16>(wfmt);
   }
 }
 
@@ -1184,14 +1141,37 @@ void free_engine(amk_engine* e) {
 
 // The kernel derives every address from (type, params) and the standard
 // buffer layout; refuse descriptions it cannot execute exactly as validated.
+// output rows a projection task holds in LDS (0 for the other task types)
+int64_t task_res_rows(const Task& t) {
+  switch (t.type) {
+    case AMK_TASK_QKV: return 2 * ((int64_t)t.p[2] - t.p[1]);
+    case AMK_TASK_GATEUP: return 2 * ((int64_t)t.p[2] - t.p[1]);
+    case AMK_TASK_OPROJ:
+    case AMK_TASK_DOWN: return (int64_t)t.p[2] - t.p[1];
+    case AMK_TASK_LMHEAD: return (int64_t)t.p[1] - t.p[0];
+    default: return 0;
+  }
+}
+
 amk_status check_executable(const amk_schedule& s) {
+  amk_schedule_config rc;
+  if (resolve_config(s.model, s.config, &rc) != AMK_OK) return AMK_ERR_UNSUPPORTED;
+  if (std::memcmp(&rc, &s.config, sizeof rc) != 0)
+    return fail(AMK_ERR_UNSUPPORTED, "schedule config is not in resolved form");
+  if ((int64_t)s.queues.size() != s.config.num_cus)
+    return fail(AMK_ERR_UNSUPPORTED, "queue count differs from num_cus");
   const std::vector<Buffer> std_buffers = buffer_table(s.model, s.config.attn_splits);
   if (s.buffers.size() != std_buffers.size())
     return fail(AMK_ERR_UNSUPPORTED, "buffer table differs from the library layout");
   for (size_t b = 0; b < std_buffers.size(); ++b)
     if (s.buffers[b].size != std_buffers[b].size || s.buffers[b].kind != std_buffers[b].kind)
       return fail(AMK_ERR_UNSUPPORTED, "buffer table differs from the library layout");
+  const int64_t kmax = std::max({(int64_t)s.model.hidden, (int64_t)s.model.ffn,
+                                 (int64_t)s.model.n_heads * s.model.head_dim});
   for (const Task& t : s.tasks) {
+    // a task's weight rows are addressed with 32-bit buffer offsets
+    if (task_res_rows(t) * kmax * 2 + 4096 > ((int64_t)1 << 31))
+      return fail(AMK_ERR_UNSUPPORTED, "a task's weight rows exceed 2 GiB");
     if ((int)t.waits.size() > kMaxWaits || (int)t.sigs.size() > kMaxSigs)
       return fail(AMK_ERR_UNSUPPORTED, "a task has more than 4 waits or signals");
     if ((t.type == AMK_TASK_ATTN && t.p[3] != s.config.attn_splits) ||
@@ -1246,24 +1226,24 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   // ---- LDS plan (floats)
   const int64_t H = m.hidden, F = m.ffn, qd = (int64_t)m.n_heads * m.head_dim, hd = m.head_dim;
   const int64_t kmax = std::max({H, F, qd});
-  const int64_t xs_floats = ((kmax + 2047) / 2048) * 2048 + ((kmax + 2047) / 2048) * 64;  // x + int4 chunk sums
-  auto max_rows = [](int64_t n, int64_t T) { return (n + T - 1) / T; };
-  const int64_t res_floats = std::max({2 * max_rows((int64_t)(m.n_heads + 2 * m.n_kv_heads) * hd / 2, c.tiles_qkv),
-                                       max_rows(H, c.tiles_o), 2 * max_rows(F, c.tiles_gateup),
-                                       max_rows(H, c.tiles_down), max_rows(m.vocab, c.tiles_lm)});
-  const int64_t grp = m.n_heads / m.n_kv_heads, gb = std::min<int64_t>(grp, 4);
-  const int64_t maxlen = 0;
-  const int64_t att_floats = std::max<int64_t>(kWaves * 64 * 10, (int64_t)c.attn_splits * (hd + 1));
+  const int64_t E = m.wfmt == AMK_W_BF16 ? 8 : (m.wfmt == AMK_W_INT8_ROW ? 16 : 32);
+  const int64_t padded = (kmax + E * 64 - 1) / (E * 64) * (E * 64);
+  const int64_t xs_floats = padded + padded / 32;  // x + int4 chunk sums
+  int64_t res_rows = 1;
+  for (const Task& t : s->tasks) res_rows = std::max(res_rows, task_res_rows(t));
+  const int64_t res_floats = (res_rows + 3) / 4 * 4;
+  const int64_t tbl_floats = res_floats * kWaves;
+  const int64_t att_floats = std::max<int64_t>(kWaves * 64 * 10 + 4 * (hd + 2), (int64_t)c.attn_splits * (hd + 1));
   const int64_t head = 16;  // block-reduction slots + flag + int8 sum
   const int64_t lds_x = head, lds_res = lds_x + xs_floats;
   const int64_t lds_att = head;
-  const int64_t total_floats = std::max(lds_res + ((res_floats + 3) / 4) * 4, lds_att + att_floats);
+  const int64_t total_floats = std::max(lds_res + res_floats + tbl_floats, lds_att + att_floats);
   e->lds_bytes = (size_t)total_floats * 4;
   if (e->lds_bytes > (size_t)prop.sharedMemPerBlock)
     return (free_engine(e), fail(AMK_ERR_UNSUPPORTED, "schedule needs " + std::to_string(e->lds_bytes) +
                                                           " bytes of LDS per workgroup; device allows " +
                                                           std::to_string(prop.sharedMemPerBlock)));
-  e->kernel = kernel_for_depth(c.pipeline_depth);
+  e->kernel = kernel_for(c.pipeline_depth, m.wfmt);
   if (e->lds_bytes > 65536) {
     hipError_t err = hipFuncSetAttribute(e->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds_bytes);
     if (err != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(err)));
@@ -1291,6 +1271,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     DevTask d{};
     d.type = t.type;
     d.id = (int32_t)i;
+    d.qslot = 0;
     d.nwait = (int32_t)t.waits.size();
     d.nsig = (int32_t)t.sigs.size();
     std::copy(t.p, t.p + 8, d.p);
@@ -1302,6 +1283,8 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     for (size_t k = 0; k < t.sigs.size(); ++k) d.sctr[k] = t.sigs[k];
     dt[i] = d;
   }
+  for (const auto& q : s->queues)
+    for (size_t k = 0; k < q.size(); ++k) dt[q[k]].qslot = (int32_t)(k & 1);
   std::vector<int32_t> qoff(1, 0), queue;
   for (const auto& q : s->queues) {
     queue.insert(queue.end(), q.begin(), q.end());
@@ -1358,7 +1341,9 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   pr.lds_x = (int32_t)lds_x;
   pr.lds_res = (int32_t)lds_res;
   pr.lds_att = (int32_t)lds_att;
-  pr.att_maxlen = (int32_t)maxlen;
+  pr.res_floats = (int32_t)res_floats;
+  pr.poll_late = c.poll_mode;
+  pr.rel0 = c.release_mode;
   pr.spin_ticks = (uint64_t)2000000 * (uint64_t)e->wallclock_khz / 1000u;
   *out = e;
   return AMK_OK;
