@@ -15,6 +15,19 @@ with HIP events on the launch stream.  `cpu_baseline` times the oracle on a
 bounded sample of the same workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b]
+
+Helpers for the committed profiles (see the command line in each summary):
+  --prompt-kv synthetic   fill the prompt's KV rows with seeded values instead
+                          of running the prompt through the kernel (decode
+                          time does not depend on KV values); used under the
+                          counter profiler so that only the measured launches run
+  --probe copy            copy a 1 GiB device buffer 5 times with torch's copy_
+                          (the runtime's device-to-device copy kernel: the
+                          known-size kernel that calibrates FETCH_SIZE and
+                          WRITE_SIZE), then exit
+  --traffic-from F W CF CW  read rocprofv3 counter CSVs (FETCH_SIZE and
+                          WRITE_SIZE of a bench run, then of a copy probe run)
+                          and write profiles/traffic_amk_vm_<workload>.json
 """
 import argparse
 import hashlib
@@ -63,6 +76,49 @@ def load_traffic(workload, nsteps_bytes):
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30
+
+
+def _counter_rows(path, counter):
+    """(kernel name, value) per dispatch of one counter from a rocprofv3
+    counter_collection CSV."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_from(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of the megakernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the ratio of known bytes to counted
+    bytes of a plain device copy of COPY_BYTES (read COPY_BYTES, write
+    COPY_BYTES)."""
+    def med(rows, pat):
+        v = [x for k, x in rows if pat in k]
+        assert v, f"no dispatch of a kernel matching {pat!r}"
+        return float(np.median(v)), len(v)
+    copy_pat = "copyBuffer"  # the runtime's device-to-device copy kernel behind torch's copy_
+    cf, ncf = med(_counter_rows(copy_fetch_csv, "FETCH_SIZE"), copy_pat)
+    cw, ncw = med(_counter_rows(copy_write_csv, "WRITE_SIZE"), copy_pat)
+    kf, nkf = med(_counter_rows(fetch_csv, "FETCH_SIZE"), "amk_vm")
+    kw, nkw = med(_counter_rows(write_csv, "WRITE_SIZE"), "amk_vm")
+    fscale = COPY_BYTES / (cf * 1024.0)
+    wscale = COPY_BYTES / (cw * 1024.0)
+    out = {"workload": workload, "kernel_sha256_16": kernel_hash(),
+           "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES,
+           "fetch_scale": fscale, "write_scale": wscale,
+           "dispatches": {"kernel_fetch": nkf, "kernel_write": nkw, "copy_fetch": ncf, "copy_write": ncw},
+           "bytes_per_launch": kf * 1024.0 * fscale + kw * 1024.0 * wscale}
+    path = os.path.join(PROFILES, f"traffic_amk_vm_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def cpu_baseline(wl, weights, budget_s=20.0, max_steps=8):
@@ -119,8 +175,6 @@ def analyse_trace(view, stamps, khz):
         for c in t["sigs"]:
             prod.setdefault(c, []).append(i)
     lat_first, lat_med = [], []
-    for i, t in enumerate(tasks):
-        pass
     cons = {}
     for i, t in enumerate(tasks):
         for c, _ in t["waits"]:
@@ -148,7 +202,13 @@ def main():
     ap.add_argument("--depth", type=int, default=0, help="pipeline_depth override")
     ap.add_argument("--sched", default="", help="schedule overrides k=v,k=v")
     ap.add_argument("--trace", default="", help="after timing, trace 2 steps and write the analysis here")
+    ap.add_argument("--prompt-kv", choices=("decode", "synthetic"), default="decode")
+    ap.add_argument("--probe", choices=("", "copy"), default="")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(args.workload, *args.traffic_from)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path is a "
               "single-GPU persistent kernel; multi-GPU sharding is a design note, not built.",
@@ -156,6 +216,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.probe == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy", "bytes": COPY_BYTES, "launches": 5}))
+        return
 
     import persistent_megakernel_wg_amd as amk
     import synth
@@ -188,13 +257,19 @@ def main():
     toks = synth.tokens(2, wl.prompt_len + steps + args.warmup, wl.vocab)
     stream = torch.cuda.current_stream()
 
-    # prompt: teacher-forced decode steps (untimed)
+    # prompt: teacher-forced decode steps (untimed), or seeded KV rows
     t0 = time.time()
-    for p in range(wl.prompt_len):
-        eng.decode_step(int(toks[p]), p, stream)
+    if args.prompt_kv == "synthetic":
+        kvp = synth.kv_prefix(wl, wl.prompt_len, seed=3)
+        kv.copy_(torch.from_numpy(kvp.view(np.int16).reshape(-1)).to(dev))
+        del kvp
+        eng.set_kv_length(wl.prompt_len)
+    else:
+        for p in range(wl.prompt_len):
+            eng.decode_step(int(toks[p]), p, stream)
     torch.cuda.synchronize()
     eng.check()
-    log(f"prompt of {wl.prompt_len} positions in {time.time() - t0:.2f}s")
+    log(f"prompt of {wl.prompt_len} positions ({args.prompt_kv}) in {time.time() - t0:.2f}s")
     P = wl.prompt_len
     # warmup steps, then rewind so that the timed steps see the workload's positions
     for i in range(args.warmup):
@@ -202,22 +277,25 @@ def main():
     torch.cuda.synchronize()
     eng.check()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # HIP events on the launch stream right before and after every launch:
+    # their difference is the kernel's duration (the roofline's denominator)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     dec = toks[P + args.warmup:]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev[0].record(stream)
     for i in range(steps):
+        ev0[i].record(stream)
         eng.decode_step(int(dec[i]), P + i, stream)
-        ev[i + 1].record(stream)
+        ev1[i].record(stream)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     eng.check()
-    lat = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)])  # seconds
+    lat = np.array([ev0[i].elapsed_time(ev1[i]) * 1e-3 for i in range(steps)])  # seconds
     gpu_total = float(lat.sum())
     B = np.array([step_bytes(amk, model, P + i) for i in range(steps)], dtype=np.float64)
     tmin = B / HBM_PEAK
-    floor_frac = float(tmin.sum() / gpu_total)
+    floor_frac = float(tmin.sum() / (t_total))
     achieved = float(B.mean() / lat.mean())
     traffic = load_traffic(wl.name, B.mean())
     out = {
@@ -240,8 +318,9 @@ def main():
                    "batch": 1, "prompt_len": P, "decode_steps": steps,
                    "schedule": cfg.as_dict()},
         "floor_fraction": floor_frac,
+        "floor_fraction_kernel": float(tmin.sum() / gpu_total),
         "t_min_ms_mean": float(tmin.mean() * 1e3),
-        "latency_ms": {"mean": float(lat.mean() * 1e3), "median": float(np.median(lat) * 1e3),
+        "kernel_ms": {"mean": float(lat.mean() * 1e3), "median": float(np.median(lat) * 1e3),
                        "p90": float(np.percentile(lat, 90) * 1e3), "min": float(lat.min() * 1e3)},
         "bytes_per_step_mean": float(B.mean()),
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
