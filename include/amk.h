@@ -119,6 +119,37 @@ typedef enum {
 #define AMK_ACCESS_READ 1
 #define AMK_ACCESS_WRITE 2
 
+/* Buffers of a schedule built by amk_build_schedule (ids in a schedule view):
+ *   0 embedding (packed tensor 0)    1 final norm (packed 1)   2 LM head (packed 2)
+ *   3 KV history [L][2][nkv][max_ctx][hd] bf16     4 KV row of this step [L][2][nkv][hd] bf16
+ *   5 logits fp32 [V]     6 x fp32 [L][2][H] (after attention, after MLP of layer l)
+ *   7 q fp32 [L][nq][hd]  8 attention partials fp32 [L][nq][S][hd + 2]
+ *   9 o fp32 [L][nq][hd]  10 a fp32 [L][F]
+ *   11 + 6l + {0 attn norm, 1 qkv, 2 o, 3 mlp norm, 4 gate/up, 5 down}: packed 3 + 6l + ...
+ * Byte ranges [begin, end) that a typed task declares (and the safety gate
+ * re-derives), with x_in(l, r0, r1) = all of buffer 0 when l = 0, else x of
+ * layer l-1 "after MLP" rows [r0, r1); "rows [a, b) of packed tensor T" =
+ * data bytes [a*rb, b*rb) plus, for int8 / int4, meta bytes [D + a*mb, D + b*mb)
+ * (rb, mb = data and meta bytes per row, D = rows*rb):
+ *   QKV (l, u0, u1): read x_in(l, 0, H), attn norm (all), rows [2u0, 2u1) of qkv;
+ *     per head slot hs touched by units [u0, u1) (unit u = hs*hd/2 + i), with
+ *     i in [i0, i1): write q[l][hs] (hs < nq) or the KV row of layer l, K for
+ *     slot nq..nq+nkv-1, V after (slot g), elements [i0, i1) and
+ *     [hd/2 + i0, hd/2 + i1), as two ranges.
+ *   ATTN (l, g, s, S): read q[l][g*grp .. (g+1)*grp) (grp = nq/nkv), per
+ *     K then V: history rows of (l, K/V, g) (all max_ctx) and the KV row of
+ *     (l, K/V, g); write partial (l, h, s) for each h of the group.
+ *   MERGE (l, h, S): read partials (l, h, 0..S); write o[l][h].
+ *   OPROJ (l, r0, r1): read o[l] (all), x_in(l, r0, r1), rows [r0, r1) of o;
+ *     write x[l][0] rows [r0, r1).
+ *   GATEUP (l, j0, j1): read x[l][0] (all), mlp norm (all), rows [2j0, 2j1)
+ *     of gate/up; write a[l] [j0, j1).
+ *   DOWN (l, r0, r1): read a[l] (all), x[l][0] rows [r0, r1), rows [r0, r1)
+ *     of down; write x[l][1] rows [r0, r1).
+ *   LMHEAD (r0, r1): read x[L-1][1] (all), final norm (all), rows [r0, r1)
+ *     of the LM head; write logits [r0, r1).
+ * Params out of range (layer, head, split, rows) make the task invalid (REF). */
+
 typedef struct { int32_t type, cu; int32_t p[8]; } amk_task_desc;
 typedef struct { int32_t counter; uint32_t threshold; } amk_wait_desc;
 typedef struct { int32_t buffer, mode; int64_t begin, end; } amk_access_desc; /* bytes [begin,end) */
