@@ -219,10 +219,24 @@ amk_status amk_default_schedule_config(const amk_model_config* model, int32_t de
 amk_status amk_build_schedule(const amk_model_config* model, const amk_schedule_config* config,
                               amk_schedule** out);
 
-/* The static safety gate (AMK summary, "Methodology", "The safety gate";
- * rules and their order in the design doc).  AMK_OK iff the schedule is safe, else
- * AMK_ERR_UNSAFE_SCHEDULE with *out naming the first failure.  Host only,
- * never touches a GPU. */
+/* The static safety gate (AMK summary, "Methodology", "The safety gate"),
+ * rules checked in this order, the first failure reported:
+ *   V1 REF: queue entries name tasks; each task sits in exactly one queue,
+ *      that of its cu; counters, buffers, modes and byte ranges in range;
+ *      a typed task declares exactly the accesses listed above.
+ *   V2 THRESHOLD: every wait (C, t) has 1 <= t <= P(C), P(C) = number of
+ *      signal entries naming C.
+ *   V3 CYCLE: producer -> waiter edges are acyclic.
+ *   V4 QUEUE_ORDER: producer -> waiter edges plus queue edges are acyclic.
+ *   V5 UNDER_JOINED: a partial wait (t < P(C)) by a task that reads bytes a
+ *      producer of C writes.
+ *   V6 RACE: overlapping accesses of two tasks, one a write, not ordered by
+ *      happens-before (queue edges and full-join producer -> waiter edges).
+ *   V7 OUTPUT: each OUTPUT buffer fully written, and every task reaches,
+ *      through happens-before-ordered writer -> reader data flow, a task
+ *      writing an OUTPUT or STATE buffer.
+ * AMK_OK iff the schedule is safe, else AMK_ERR_UNSAFE_SCHEDULE with *out
+ * naming the first failure.  Host only, never touches a GPU. */
 amk_status amk_validate(const amk_schedule* schedule, amk_verdict* out);
 
 /* Flat view of a schedule; the arrays stay valid until amk_schedule_free. */
@@ -250,9 +264,11 @@ amk_status amk_packed_bytes(const amk_model_config* model, int32_t k, size_t* by
  * Face [out][in] order (0 embedding, 1 + 9l + {0 attn_norm, 1 wq, 2 wk, 3 wv,
  * 4 wo, 5 mlp_norm, 6 w_gate, 7 w_up, 8 w_down}, 1 + 9L final_norm,
  * 2 + 9L lm_head, unused when tied); only the ids packed tensor k needs are
- * read.  dst is host memory of amk_packed_bytes bytes.  Quantisation follows
- * the formats in the design doc (int8: s = amax/127 per row; int4: groups of 128,
- * s = fp16((max-min)/15), z = round(-min/s)), computed in fp32. */
+ * read.  dst is host memory of amk_packed_bytes bytes.  Quantisation, in
+ * fp32 with round-half-even: int8 per output row s = amax/127 (all-zero
+ * row: s = 1), q = clamp(round(w/s), -127, 127); int4 per group of 128
+ * input columns s = fp16((max - min)/15) (0 -> 1), z = clamp(round(-min/s),
+ * 0, 15), q = clamp(round(w/s) + z, 0, 15). */
 amk_status amk_pack_tensor(const amk_model_config* model, int32_t k,
                            const uint16_t* const* canonical, void* dst);
 

@@ -10,7 +10,7 @@
 // Argus page's megakernel case study (section "Workload and baselines": GEMM,
 // attention, normalisation, KV-cache update and logits of one decode step).
 // The pages give no formulas for these operators; the plain Llama
-// definitions are used, with the readings listed in the design doc:
+// definitions are used, read as follows:
 //   * RMSNorm:  y_i = x_i / sqrt(mean(x^2) + eps) * g_i
 //   * RoPE:     rotate-half pairs (i, i + hd/2), angle pos * theta^(-2i/hd)
 //   * attention: causal over positions 0..pos inclusive, scale 1/sqrt(hd),

@@ -341,7 +341,7 @@ def pack_tensor(model, k, canonical, out=None):
 
 def unpack_tensor(model, k, canonical_id, packed, rows, cols):
     """Canonical quantised values of one projection inside packed tensor k."""
-    fmt = model.wfmt if k != 0 and (k == 2 or (k - 3) % 6 in (1, 2, 4, 5)) else W_BF16
+    fmt = model.wfmt if k == 2 or (k >= 3 and (k - 3) % 6 in (1, 2, 4, 5)) else W_BF16
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     if fmt == W_BF16:
         q = np.empty((rows, cols), np.uint16)
