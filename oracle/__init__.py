@@ -60,6 +60,7 @@ def lib():
             "orc_model_new": ([ctypes.POINTER(OrcConfig), p], p),
             "orc_model_free": ([p], None),
             "orc_step": ([p, p, i32, i32, p], i32),
+            "orc_set_jitter": ([d, ctypes.c_uint64], None),
             "orc_model_quant": ([p, i32, p, p, p], i32),
             "orc_set_threads": ([i32], None),
             "orc_get_threads": ([], i32),
@@ -183,6 +184,13 @@ def config_of(wl):
     return OrcConfig(wl.n_layers, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.ffn,
                      wl.vocab, wl.max_ctx, wl.rms_eps, wl.rope_theta, int(wl.tied),
                      WFMT[wl.wfmt], int(wl.act_bf16))
+
+
+def set_jitter(eps, seed=0):
+    """Conditioning probe: multiply each value by 1 + eps*r (r uniform in
+    [-1, 1)) right before every bf16 rounding decision of the decoder
+    (activations of act_bf16 models, KV rows).  eps = 0 turns it off."""
+    lib().orc_set_jitter(float(eps), int(seed))
 
 
 class Model:

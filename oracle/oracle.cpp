@@ -369,9 +369,34 @@ orc_model* orc_model_new(const orc_config* c, const uint16_t* const* canon) {
 
 void orc_model_free(orc_model* m) { delete m; }
 
+// Conditioning probe (off unless set): before each rounding decision the
+// workload fixes (activation to bf16, KV row to bf16) every value is
+// multiplied by 1 + eps*r, r uniform in [-1, 1) from a SplitMix64 counter
+// stream.  With eps near the fp32 unit roundoff this shows how far the
+// logits move when those decisions are taken on values carrying fp32-sized
+// errors, which is the spread any fp32 implementation has against this
+// oracle.
+static double g_jitter_eps = 0.0;
+static uint64_t g_jitter_ctr = 0;
+
+void orc_set_jitter(double eps, uint64_t seed) {
+  g_jitter_eps = eps;
+  g_jitter_ctr = seed;
+}
+
+static double jitter(double v) {
+  if (g_jitter_eps == 0.0) return v;
+  uint64_t z = (g_jitter_ctr++) + 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  z ^= z >> 31;
+  const double r = (double)(z >> 11) * (1.0 / 9007199254740992.0) * 2.0 - 1.0;
+  return v * (1.0 + g_jitter_eps * r);
+}
+
 static void maybe_round(std::vector<double>& v, int act_bf16) {
   if (!act_bf16) return;
-  for (double& e : v) e = orc_bf16_round_trip(e);
+  for (double& e : v) e = orc_bf16_round_trip(jitter(e));
 }
 
 // One decode step at position pos for input token `token`.
@@ -397,8 +422,8 @@ int orc_step(orc_model* m, uint16_t* kv, int token, int pos, double* logits) {
       uint16_t* Kr = kv + ((((size_t)l * 2 + 0) * nkv + g) * mc + pos) * hd;
       uint16_t* Vr = kv + ((((size_t)l * 2 + 1) * nkv + g) * mc + pos) * hd;
       for (int i = 0; i < hd; ++i) {
-        Kr[i] = orc_round_bf16(k[g * hd + i]);
-        Vr[i] = orc_round_bf16(v[g * hd + i]);
+        Kr[i] = orc_round_bf16(jitter(k[g * hd + i]));
+        Vr[i] = orc_round_bf16(jitter(v[g * hd + i]));
       }
     }
 #pragma omp parallel for schedule(static)

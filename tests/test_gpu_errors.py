@@ -1,0 +1,121 @@
+"""Error paths and edge positions of the engine (runs on MI355X).
+
+Argument errors are refused on the host before any launch.  The time-out
+path is forced from the host with a tiny spin budget on the kernel's own
+bounded waits, so every workgroup still exits normally; the engine must then
+report AMK_ERR_TIMEOUT, reset its counters and decode correctly again.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import persistent_megakernel_wg_amd as amk
+import synth
+from tests.gpu_common import compare, gpu_step, log, make_engine
+from tests.validator_common import lowered
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = synth.get("tiny")
+    return wl, synth.model_weights(wl, seed=1)
+
+
+def expect_status(code, fn, *args):
+    with pytest.raises(amk.AmkError) as e:
+        fn(*args)
+    assert e.value.status == code, str(e.value)
+
+
+def test_decode_step_argument_errors(tiny):
+    wl, w = tiny
+    eng = make_engine(wl, w)
+    expect_status(amk.ERR_OUT_OF_RANGE, eng.decode_step, wl.vocab, 0)
+    expect_status(amk.ERR_OUT_OF_RANGE, eng.decode_step, -1, 0)
+    expect_status(amk.ERR_OUT_OF_RANGE, eng.decode_step, 0, wl.max_ctx)
+    expect_status(amk.ERR_INVALID_ARG, eng.decode_step, 0, 1)      # gap: nothing written yet
+    gpu_step(eng, 3, 0)
+    expect_status(amk.ERR_INVALID_ARG, eng.decode_step, 0, 2)      # gap after one position
+    expect_status(amk.ERR_OUT_OF_RANGE, eng.set_kv_length, wl.max_ctx + 1)
+    eng.close()
+
+
+def test_engine_refuses_unsafe_and_foreign_schedules(tiny):
+    import torch
+    wl, w = tiny
+    m = amk.ModelConfig.from_workload(wl)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = lowered(m, num_cus=cus)
+    dev_w = amk.upload_model(m, w)
+    kv, logits = amk.alloc_state(m)
+    # a wait removed from a consumer: the gate refuses the schedule (race)
+    bad = {**s, "tasks": [dict(t) for t in s["tasks"]]}
+    i = next(k for k, t in enumerate(bad["tasks"]) if t["type"] == 4 and t["waits"])
+    bad["tasks"][i] = {**bad["tasks"][i], "waits": []}
+    bad["model"] = m
+    sch = amk.Schedule.from_dict(bad)
+    assert sch.validate()[0] != 0
+    expect_status(amk.ERR_UNSAFE_SCHEDULE, amk.Engine, sch, dev_w, kv, logits)
+    # a safe schedule whose config is not the resolved one the lowering used
+    good = {**s, "model": m}
+    cfg = amk.default_schedule_config(m, cus)
+    cfg.pipeline_depth = 0
+    good["config"] = cfg
+    sch = amk.Schedule.from_dict(good)
+    assert sch.validate()[0] == 0
+    expect_status(amk.ERR_UNSUPPORTED, amk.Engine, sch, dev_w, kv, logits)
+
+
+def test_timeout_is_reported_and_the_engine_recovers(tiny):
+    wl, w = tiny
+    toks = synth.tokens(2, 12, wl.vocab)
+    eng = make_engine(wl, w)
+    orc = oracle.Model(wl, w)
+    kv_o = orc.new_kv()
+    for p in range(8):
+        gpu_step(eng, int(toks[p]), p)
+        orc.step(kv_o, int(toks[p]), p)
+    log("forcing a time-out with a 1 us spin budget")
+    eng.set_spin_budget(1)
+    eng.decode_step(int(toks[8]), 8)
+    import torch
+    torch.cuda.synchronize()
+    expect_status(amk.ERR_TIMEOUT, eng.check)
+    eng.check()  # the error was consumed and the counters restarted
+    eng.set_spin_budget(2_000_000)
+    for p in range(8, 12):  # position 8 again (rewind onto the aborted row), then onwards
+        g = gpu_step(eng, int(toks[p]), p)
+        o = orc.step(kv_o, int(toks[p]), p)
+        rel, mab, same = compare(g, o)
+        assert rel <= 1e-2 and mab <= 2e-2 and same, (p, rel, mab)
+    eng.close()
+
+
+def test_last_position_and_rewind(tiny):
+    """Decode up to the last cache position, then rewind to an earlier one and
+    decode a different continuation: both match the oracle."""
+    wl, w = tiny
+    n = wl.max_ctx
+    toks = synth.tokens(4, n, wl.vocab)
+    alt = synth.tokens(5, 6, wl.vocab)
+    eng = make_engine(wl, w)
+    orc = oracle.Model(wl, w)
+    kv_o = orc.new_kv()
+    worst = 0.0
+    for p in range(n):
+        g = gpu_step(eng, int(toks[p]), p)
+        o = orc.step(kv_o, int(toks[p]), p)
+        rel, mab, same = compare(g, o)
+        worst = max(worst, rel)
+        assert rel <= 1e-2 and mab <= 2e-2 and same, (p, rel)
+    log(f"tiny to pos {n - 1}: worst relL2 {worst:.2e}")
+    r = 20
+    kv_o[:, :, :, r:, :] = 0
+    for i, tok in enumerate(alt):
+        g = gpu_step(eng, int(tok), r + i)
+        o = orc.step(kv_o, int(tok), r + i)
+        rel, mab, same = compare(g, o)
+        assert rel <= 1e-2 and mab <= 2e-2 and same, (r + i, rel)
+    eng.close()

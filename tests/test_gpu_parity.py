@@ -53,6 +53,8 @@ def test_1b_tied_short_and_long():
 
 @pytest.fixture(scope="module")
 def w8b():
+    """Seeded bf16 weights of the 8B shape; the int8 / int4 workloads quantise
+    these same tensors (both sides quantise with their own code)."""
     wl = synth.get("8b")
     log("generating 8b weights")
     return synth.model_weights(wl, seed=1)
@@ -66,7 +68,7 @@ def _free():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["8b"])
+@pytest.mark.parametrize("name", ["8b", "8b_int8", "8b_int4"])
 def test_full_size_short_prompt(name, w8b):
     """Full-size model, launch configuration of the bench: a 3-token prompt
     and 3 decode steps, every step compared with the oracle."""
@@ -75,14 +77,15 @@ def test_full_size_short_prompt(name, w8b):
     res, eng, _ = teacher_forced(wl, w8b, toks)
     del eng
     _free()
-    agree, rel, mab = check_run(res, min_argmax=1.0)
+    agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
     log(f"{name} short: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
 
 
-@pytest.mark.parametrize("name", ["8b"])
+@pytest.mark.parametrize("name", ["8b", "8b_int8", "8b_int4"])
 def test_full_size_long_context(name, w8b):
-    """Full-size model after the workload's prompt length: the KV cache holds
-    seeded rows 0..P-1 (same bytes on both sides), then 2 decode steps."""
+    """Full-size model after the workload's prompt length (1024 positions; 8192
+    for int4): the KV cache holds seeded rows 0..P-1 (same bytes on both
+    sides), then 2 decode steps."""
     wl = synth.get(name)
     P = wl.prompt_len
     kvp = synth.kv_prefix(wl, P, seed=3)
@@ -90,5 +93,5 @@ def test_full_size_long_context(name, w8b):
     res, eng, _ = teacher_forced(wl, w8b, toks, kv_prefix=kvp, start=P)
     del eng
     _free()
-    agree, rel, mab = check_run(res, min_argmax=1.0)
+    agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
     log(f"{name} long: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
