@@ -82,10 +82,13 @@ typedef struct {
    * poll_mode 0: the polling wave issues its weight prologue before the
    *   wait like the others; 1: after the wait (its poll is then not queued
    *   behind its own loads).
+   * prefetch_kb: LDS kilobytes per task into which the end of the previous
+   *   task of the queue copies the task's first weight slabs (LDS DMA), so
+   *   streaming goes on through waits; 0 = all that fits, -1 = off.
    * release_mode 0: all waves wait for their stores, barrier, then the
    *   release; 1: the epilogue stores and the release are issued by the
    *   polling wave alone while the others start the next task. */
-  int32_t poll_mode, release_mode;
+  int32_t poll_mode, release_mode, prefetch_kb;
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */

@@ -121,15 +121,25 @@ constexpr int kMaxWaits = 4;
 constexpr int kMaxSigs = 4;
 constexpr int kCounterStride = 32;  // u32 per counter: one 128-byte line each
 
-struct alignas(16) DevTask {
-  int32_t type, nwait, nsig, id;
-  int32_t p[8];
+// One 128-byte line per task (the table is 128-byte aligned), with every
+// field the wait and the signal read in it.
+struct alignas(128) DevTask {
+  int32_t type, id;
+  int8_t nwait, nsig;
+  int8_t qslot;    // parity of the task's position in its queue (wait-flag slot)
+  int8_t pf_have;  // weight steps per wave already in LDS when the task starts (0: none)
+  int32_t pf_lds;  // LDS byte offset of that prefetch area (wave w at + w*pf_have*step bytes)
+  int32_t p[6];    // task params (typed tasks use at most 4)
   int32_t wctr[kMaxWaits];
   uint32_t wthr[kMaxWaits];
   uint32_t wprod[kMaxWaits];  // producers of the counter (epoch stride)
   int32_t sctr[kMaxSigs];
-  int32_t qslot;  // parity of the task's position in its queue (wait-flag slot)
-  int32_t pad1[3];
+  // weights this task prefetches for the next task of its queue, after its
+  // signal: packed tensor, rows per unit, steps per wave (0: none), inputs per
+  // row, LDS byte offset, first row, units, rows of the whole tensor
+  int16_t pfn_tensor;
+  int8_t pfn_rpu, pfn_steps;
+  int32_t pfn_K, pfn_lds, pfn_row0, pfn_nunits, pfn_rows_total;
 };
 static_assert(sizeof(DevTask) == 128, "device task record is 128 bytes");
 

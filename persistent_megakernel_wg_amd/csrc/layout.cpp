@@ -66,6 +66,9 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.poll_mode != 0 && c.poll_mode != 1) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0 or 1");
   if (c.release_mode != 0 && c.release_mode != 1)
     return fail(AMK_ERR_UNSUPPORTED, "release_mode must be 0 or 1");
+  if (c.prefetch_kb == 0) c.prefetch_kb = 160;
+  if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
+    return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");
   if (c.fuse_flags == 0) c.fuse_flags = AMK_FUSE_DEFAULT;
   if (c.fuse_flags != AMK_FUSE_DEFAULT)
     return fail(AMK_ERR_UNSUPPORTED, "only the fully fused task set (AMK_FUSE_DEFAULT) is built");

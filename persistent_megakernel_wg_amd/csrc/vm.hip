@@ -34,8 +34,15 @@ namespace amk {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+constexpr int kHead = 16;  // LDS floats: block-reduction slots, wait flags, int8 sum of x
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr uint32_t kOob = 0x80000000u;       // offset past every descriptor range
+
+// Task records are read-only for the whole launch: reading them through the
+// constant address space lets the compiler use scalar loads (scalar cache,
+// counted apart from the vector loads that stream weights).
+typedef const __attribute__((address_space(4))) DevTask CTask;
+typedef CTask& TaskRef;
 
 struct VmParams {
   const DevTask* tasks;
@@ -58,8 +65,9 @@ struct VmParams {
   uint32_t epoch;
   int32_t L, H, nq, nkv, hd, F, V, mc, S, wfmt, act_bf16;
   float eps;
-  // LDS carve-up (float offsets into dynamic shared memory)
-  int32_t lds_x, lds_res, lds_att, res_floats;
+  // LDS offset (floats) of the attention scratch; GEMV tasks place x at
+  // kHead and their partial tables right after (xs_floats)
+  int32_t lds_att;
   // queue-walk knobs of the schedule configuration
   int32_t poll_late;  // the polling wave issues its weight prologue after the wait
   int32_t rel0;       // epilogue stores and release by wave 0 alone
@@ -203,7 +211,8 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // workgroup already reported an error (the launch then drains).  The flag
 // slot alternates with the task's queue position: waves that run ahead into
 // the next task cannot overwrite a flag a slower wave has yet to read.
-__device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int* flags) {
+template <typename Hook>
+__device__ __forceinline__ bool vm_wait(const VmParams& P, TaskRef t, int* flags, Hook&& before_barrier) {
   int* flag = flags + t.qslot;
   if (opaque_tid() == 0) {
     if (P.trace) P.trace[(size_t)t.id * 4 + 0] = wall_clock64();
@@ -229,8 +238,13 @@ __device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int
     *flag = ok;
     if (P.trace) P.trace[(size_t)t.id * 4 + 1] = wall_clock64();
   }
+  before_barrier();
   __syncthreads();
   return *flag != 0;
+}
+
+__device__ __forceinline__ bool vm_wait(const VmParams& P, TaskRef t, int* flags) {
+  return vm_wait(P, t, flags, [] {});
 }
 
 // Release.  Every store another workgroup reads is a write-through
@@ -242,7 +256,7 @@ __device__ __forceinline__ bool vm_wait(const VmParams& P, const DevTask& t, int
 // issue the next task's weight loads.
 __device__ __forceinline__ int epilogue_threads(const VmParams& P) { return P.rel0 ? 64 : kThreads; }
 
-__device__ __forceinline__ void vm_signal(const VmParams& P, const DevTask& t) {
+__device__ __forceinline__ void vm_signal(const VmParams& P, TaskRef t) {
   const int tid = opaque_tid();
   if (!P.rel0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -443,36 +457,23 @@ __device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* 
   }
 }
 
-template <class F, int DS, int RPU, typename StageFn>
-__device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
-                                     uint32_t meta_row_bytes, int nunits, int K, const float* xs,
-                                     const float* csum, float* tbl, bool poll_late, StageFn&& stage) {
-  const int tid = opaque_tid(), lane = tid & 63;
-  const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nchunk = K / F::E;
-  const int J = (nchunk + 63) >> 6;
-  const int jl = (nchunk - lane + 63) >> 6;  // slabs in which this lane has data
-  const GemvSplit sp(nunits, J);
-  int t_unit, t_j0, t_len;
-  sp.tail(sw, &t_unit, &t_j0, &t_len);
-  const int nA = sp.nr * J;   // steps in rounds
-  const int n = nA + t_len;   // steps of this wave
-  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
-  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, F::kMeta ? (uint32_t)nunits * RPU * meta_row_bytes : 0u);
-  // issue state: steps issued, unit and slab of the next step
-  int ik = 0, iu = nA ? sw : t_unit, ij = nA ? 0 : t_j0;
-  u32x4 buf[DS][RPU];
-  uint32_t mbuf[DS][RPU];
-  auto issue = [&](u32x4 (&b)[RPU], uint32_t (&mb)[RPU]) {
-    const bool valid = ik < n && ij < jl;
-    const uint32_t off = (uint32_t)iu * RPU * row_bytes + (uint32_t)(ij * 64 + lane) * 16u;
-    const uint32_t moff = (uint32_t)iu * RPU * meta_row_bytes + (uint32_t)(ij * 16 + (lane >> 2)) * 4u;
-#pragma unroll
-    for (int r = 0; r < RPU; ++r) {
-      b[r] = bload(rs, valid ? off + (uint32_t)r * row_bytes : kOob);
-      if constexpr (F::kMeta)
-        mb[r] = __builtin_amdgcn_raw_buffer_load_b32(rm, valid ? moff + (uint32_t)r * meta_row_bytes : kOob, 0, 0);
-    }
+// Issue order of one wave's steps: its round units (sw, sw + 8, ...) slab by
+// slab, then its tail piece.  ik counts steps, (iu, ij) is the next step.
+struct StepIter {
+  int J, nA, t_unit, t_j0, n;
+  int ik, iu, ij;
+  __device__ __forceinline__ void init(int sw, int nunits, int J_) {
+    J = J_;
+    const GemvSplit sp(nunits, J);
+    int t_len;
+    sp.tail(sw, &t_unit, &t_j0, &t_len);
+    nA = sp.nr * J;
+    n = nA + t_len;
+    ik = 0;
+    iu = nA ? sw : t_unit;
+    ij = nA ? 0 : t_j0;
+  }
+  __device__ __forceinline__ void advance() {
     ++ik;
     if (++ij == J) {
       ij = 0;
@@ -482,6 +483,66 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
       iu = t_unit;
       ij = t_j0;
     }
+  }
+};
+
+// bytes of one row's slab in a prefetch area: 1 KB of weights, for int4 also
+// the 64 lanes' group meta words
+template <class F>
+constexpr uint32_t pf_row_step() { return 1024u + (F::kMeta ? 256u : 0u); }
+
+// LDS DMA of 16 (4) bytes per lane from a buffer offset to LDS byte address
+// `lds` + 16 (4) * lane.  The compiler does not see these loads: callers wait
+// for them with explicit vmcnt waits.  M0 is saved and restored around the
+// instruction.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds), "v"(off), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "s"(lds), "v"(off), "s"(r)
+               : "memory");
+}
+
+// The GEMV proper.  The first `pf_steps` steps of every wave (fewer if the
+// wave has fewer) are already in LDS at `pf` (copied there by the end of the
+// previous task, see issue_prefetch); the register ring starts after them.
+template <class F, int DS, int RPU, typename StageFn>
+__device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
+                                     uint32_t meta_row_bytes, int nunits, int K, const float* xs,
+                                     const float* csum, float* tbl, bool poll_late, int pf_steps,
+                                     const uint8_t* pf, StageFn&& stage) {
+  const int tid = opaque_tid(), lane = tid & 63;
+  const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nchunk = K / F::E;
+  const int J = (nchunk + 63) >> 6;
+  const int jl = (nchunk - lane + 63) >> 6;  // slabs in which this lane has data
+  StepIter it;
+  it.init(sw, nunits, J);
+  const int n = it.n;                // steps of this wave
+  const int np = min(pf_steps, n);   // of which prefetched
+  for (int k = 0; k < np; ++k) it.advance();
+  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * row_bytes);
+  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, F::kMeta ? (uint32_t)nunits * RPU * meta_row_bytes : 0u);
+  u32x4 buf[DS][RPU];
+  uint32_t mbuf[DS][RPU];
+  auto issue = [&](u32x4 (&b)[RPU], uint32_t (&mb)[RPU]) {
+    const bool valid = it.ik < n && it.ij < jl;
+    const uint32_t off = (uint32_t)it.iu * RPU * row_bytes + (uint32_t)(it.ij * 64 + lane) * 16u;
+    const uint32_t moff = (uint32_t)it.iu * RPU * meta_row_bytes + (uint32_t)(it.ij * 16 + (lane >> 2)) * 4u;
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) {
+      b[r] = bload(rs, valid ? off + (uint32_t)r * row_bytes : kOob);
+      if constexpr (F::kMeta)
+        mb[r] = __builtin_amdgcn_raw_buffer_load_b32(rm, valid ? moff + (uint32_t)r * meta_row_bytes : kOob, 0, 0);
+    }
+    it.advance();
   };
   auto prologue = [&] {
 #pragma unroll
@@ -495,36 +556,47 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
   stage();
   if (late) prologue();
   if (n > 0) {
-    const int iters = (n + DS - 1) / DS;
-    int ck = 0, cu = nA ? sw : t_unit, cj = nA ? 0 : t_j0;
+    StepIter c;
+    c.init(sw, nunits, J);
+    int ck = 0;
     float acc[RPU];
 #pragma unroll
     for (int r = 0; r < RPU; ++r) acc[r] = 0.0f;
-    for (int it = 0; it < iters; ++it) {
+    auto consume = [&](const u32x4 (&w)[RPU], const uint32_t (&m)[RPU]) {
+#pragma unroll
+      for (int r = 0; r < RPU; ++r) acc[r] = F::dot(acc[r], w[r], m[r], xs, c.ij, lane, csum);
+      ++ck;
+      if (ck <= n && (c.ij == J - 1 || ck == n)) {  // this wave's segment of unit c.iu is complete
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const float v = wave_sum(acc[r]);
+          if (lane == 0) tbl[(c.iu * RPU + r) * kWaves + sw] = v;
+          acc[r] = 0.0f;
+        }
+      }
+      c.advance();
+    };
+    if (np > 0) {
+      const uint8_t* mine = pf + (uint32_t)sw * (uint32_t)pf_steps * RPU * pf_row_step<F>();
+      for (int s = 0; s < np; ++s) {
+        u32x4 w[RPU];
+        uint32_t m[RPU];
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const uint8_t* row = mine + (uint32_t)(s * RPU + r) * pf_row_step<F>();
+          w[r] = *reinterpret_cast<const u32x4*>(row + lane * 16);
+          m[r] = F::kMeta ? *reinterpret_cast<const uint32_t*>(row + 1024 + lane * 4) : 0u;
+        }
+        consume(w, m);
+      }
+    }
+    const int iters = (n - np + DS - 1) / DS;
+    for (int i = 0; i < iters; ++i) {
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-#pragma unroll
-        for (int r = 0; r < RPU; ++r) acc[r] = F::dot(acc[r], buf[s][r], mbuf[s][r], xs, cj, lane, csum);
+        consume(buf[s], mbuf[s]);
         __builtin_amdgcn_sched_barrier(0);
         issue(buf[s], mbuf[s]);
-        ++ck;
-        const bool unit_end = ++cj == J;
-        if (ck <= n && (unit_end || ck == n)) {  // this wave's segment of unit cu is complete
-#pragma unroll
-          for (int r = 0; r < RPU; ++r) {
-            const float v = wave_sum(acc[r]);
-            if (lane == 0) tbl[(cu * RPU + r) * kWaves + sw] = v;
-            acc[r] = 0.0f;
-          }
-        }
-        if (unit_end) {
-          cj = 0;
-          cu += kWaves;
-        }
-        if (ck == nA) {
-          cu = t_unit;
-          cj = t_j0;
-        }
       }
     }
   }
@@ -545,12 +617,23 @@ __device__ __forceinline__ float gemv_row(const float* tbl, int i, int nunits, i
   return v;
 }
 
+__device__ __forceinline__ int round4(int n) { return (n + 3) & ~3; }
+
+// LDS floats of a GEMV task's staged input (padded to whole wave-loads) plus,
+// for int4, the per-chunk sums; the partial table follows
+template <int WFMT>
+__device__ __forceinline__ int xs_floats(int K) {
+  constexpr int E = WFMT == AMK_W_BF16 ? 8 : (WFMT == AMK_W_INT8_ROW ? 16 : 32);
+  const int padded = (K + E * 64 - 1) / (E * 64) * (E * 64);
+  return round4(padded + padded / 32);
+}
+
 // Runs the projection rows [row0, row0 + nunits*RPU) of packed tensor `ptr`
 // (rows_total rows of K inputs) on the input vector `src` (RMSNorm'd with
 // `gain` when NORM), waiting for the task's counters after the first weight
 // loads are issued.  Results: res[i] for i < nunits*RPU (LDS).
 template <int DEPTH, int WFMT, int RPU, bool SRC_BF16, bool NORM>
-__device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, float* smem, const uint8_t* ptr,
+__device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* smem, const uint8_t* ptr,
                                         int64_t rows_total, int K, int row0, int nunits, const void* src,
                                         const uint16_t* gain) {
   using F = typename std::conditional<WFMT == AMK_W_BF16, FmtBf16,
@@ -558,9 +641,9 @@ __device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, flo
   float* red = smem;                                  // kWaves floats
   int* flag = reinterpret_cast<int*>(smem + kWaves);  // two wait-flag slots
   float* xsum = smem + kWaves + 2;                    // sum of x (int8)
-  float* xs = smem + P.lds_x;
-  float* res = smem + P.lds_res;
-  float* tbl = res + P.res_floats;
+  float* xs = smem + kHead;
+  float* res = xs + xs_floats<WFMT>(K);
+  float* tbl = res + round4(nunits * RPU);
   const int padded = (K + F::E * 64 - 1) / (F::E * 64) * (F::E * 64);
   float* csum = xs + padded;  // int4: per-chunk sums of x
   const uint32_t rb = WFMT == AMK_W_BF16 ? (uint32_t)K * 2u : (WFMT == AMK_W_INT8_ROW ? (uint32_t)K : (uint32_t)K / 2u);
@@ -568,8 +651,17 @@ __device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, flo
   const uint8_t* meta = ptr + rows_total * (int64_t)rb + (int64_t)row0 * mb;
   bool ok = true;
   constexpr int DS = DEPTH / RPU;
-  gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late != 0, [&] {
-    ok = vm_wait(P, t, flag);
+  // waves 1..7 issued the LDS DMAs of this task's prefetched steps (for all
+  // waves) before its ring prologue: waiting until only the prologue's loads
+  // may be outstanding means those DMAs are done; the barrier after it shows
+  // the data to every wave.
+  constexpr int kPrologueLoads = DS * RPU * (F::kMeta ? 2 : 1);
+  const bool pf_wait = t.pf_have > 0 && opaque_tid() >= 64;
+  gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late != 0,
+                   t.pf_have, reinterpret_cast<const uint8_t*>(smem) + t.pf_lds, [&] {
+    ok = vm_wait(P, t, flag, [&] {
+      if (pf_wait) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
+    });
     if (ok) stage_x<F, SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, xsum, csum);
   });
   if (!ok) return false;
@@ -588,7 +680,7 @@ __device__ __forceinline__ bool project(const VmParams& P, const DevTask& t, flo
 // ---------------------------------------------------------------- tasks --
 
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_qkv(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], u0 = t.p[1], u1 = t.p[2];
   const int H = P.H, hd = P.hd, half = hd >> 1, nq = P.nq, nkv = P.nkv;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_QKV];
@@ -603,7 +695,7 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, fl
     ok = project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
   }
   if (!ok) return false;
-  const float* res = smem + P.lds_res;
+  const float* res = smem + kHead + xs_floats<WFMT>(H);
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
   if (tid < EW)
@@ -632,13 +724,13 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, const DevTask& t, fl
 }
 
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
   const int H = P.H, qd = P.nq * P.hd;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
   const float* src = P.o + (int64_t)l * qd;
   if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)) return false;
-  const float* res = smem + P.lds_res;
+  const float* res = smem + kHead + xs_floats<WFMT>(qd);
   float* dst = P.x + (int64_t)l * 2 * H;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
@@ -655,7 +747,7 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, const DevTask& t, 
 }
 
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_gateup(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], j0 = t.p[1], j1 = t.p[2];
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_GATEUP];
@@ -663,7 +755,7 @@ __device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t,
   const float* src = P.x + (int64_t)l * 2 * H;
   if (!project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, gain))
     return false;
-  const float* res = smem + P.lds_res;
+  const float* res = smem + kHead + xs_floats<WFMT>(H);
   float* dst = P.a + (int64_t)l * F;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
@@ -677,13 +769,13 @@ __device__ __forceinline__ bool task_gateup(const VmParams& P, const DevTask& t,
 }
 
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_down(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_down(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
   const float* src = P.a + (int64_t)l * F;
   if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)) return false;
-  const float* res = smem + P.lds_res;
+  const float* res = smem + kHead + xs_floats<WFMT>(F);
   const float* mid = P.x + (int64_t)l * 2 * H;
   float* dst = P.x + ((int64_t)l * 2 + 1) * H;
   const int tid = opaque_tid();
@@ -695,14 +787,14 @@ __device__ __forceinline__ bool task_down(const VmParams& P, const DevTask& t, f
 }
 
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_lmhead(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_lmhead(const VmParams& P, TaskRef t, float* smem) {
   const int r0 = t.p[0], r1 = t.p[1];
   const int H = P.H;
   const uint8_t* w = P.wptr[2];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
   const float* src = P.x + ((int64_t)(P.L - 1) * 2 + 1) * H;
   if (!project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)) return false;
-  const float* res = smem + P.lds_res;
+  const float* res = smem + kHead + xs_floats<WFMT>(H);
   for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
   vm_signal(P, t);
   return true;
@@ -721,7 +813,7 @@ __device__ __forceinline__ bool task_lmhead(const VmParams& P, const DevTask& t,
 // before the wait; the row at `pos` (written by this launch) is re-read after.
 // Output: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
 template <int LH, int GP, int MAXC>
-__device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, int l, int g, int h0,
+__device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, int g, int h0,
                                            int nh, int s, int S, int p0, int p1, float* smem) {
   constexpr int PW = 64 / (LH * GP);
   const int hd = P.hd, pos = P.pos, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
@@ -867,7 +959,7 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, const DevTask& t, 
 }
 
 template <int LH, int GP>
-__device__ __forceinline__ bool attn_heads(const VmParams& P, const DevTask& t, int l, int g, int s, int S,
+__device__ __forceinline__ bool attn_heads(const VmParams& P, TaskRef t, int l, int g, int s, int S,
                                            int p0, int p1, float* smem) {
   const int grp = P.nq / P.nkv;
   constexpr int MAXC = 4;
@@ -879,7 +971,7 @@ __device__ __forceinline__ bool attn_heads(const VmParams& P, const DevTask& t, 
   return true;
 }
 
-__device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_attn(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], g = t.p[1], s = t.p[2], S = t.p[3];
   const int n = P.pos + 1;
   const int p0 = (int)(((int64_t)s * n) / S), p1 = (int)(((int64_t)(s + 1) * n) / S);
@@ -923,7 +1015,7 @@ __device__ __forceinline__ bool task_attn(const VmParams& P, const DevTask& t, f
 // of loads (every thread its float4 chunks and, for threads below S, that
 // split's (max, sum)), then LDS: weights w_s = exp(m_s - M), scaled chunks
 // summed per output element in split order, o = sum / sum_s w_s l_s.
-__device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* smem) {
   const int l = t.p[0], h = t.p[1], S = t.p[2];
   int* flag = reinterpret_cast<int*>(smem + kWaves);
   float* red = smem;
@@ -995,15 +1087,87 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, const DevTask& t, 
   return true;
 }
 
-__device__ __forceinline__ bool task_nop(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool task_nop(const VmParams& P, TaskRef t, float* smem) {
   int* flag = reinterpret_cast<int*>(smem + kWaves);
   if (!vm_wait(P, t, flag)) return false;
   vm_signal(P, t);
   return true;
 }
 
+// After a task has signalled, waves 1..7 copy the first slabs of the next
+// task's weights into LDS with DMA (`t.pfn_*`, planned by the engine so the
+// area is untouched by both tasks): the slabs each wave of the next task
+// will consume first, in its own order; wave 0's slabs are issued by waves
+// 1..7 in turn, so wave 0, which polls, keeps no loads outstanding.  The
+// loads run through the next task's wait; that task waits for them before
+// its barrier (see project).
+// the prefetch fields of a task, read when the task starts so that they are
+// in registers (not a memory round trip away) when the task ends
+struct PfNext {
+  int tensor, rpu, steps, K, lds, row0, nunits, rows_total;
+  __device__ __forceinline__ explicit PfNext(TaskRef t) {
+    steps = __builtin_amdgcn_readfirstlane(t.pfn_steps);
+    tensor = __builtin_amdgcn_readfirstlane(t.pfn_tensor);
+    rpu = __builtin_amdgcn_readfirstlane(t.pfn_rpu);
+    K = __builtin_amdgcn_readfirstlane(t.pfn_K);
+    lds = __builtin_amdgcn_readfirstlane(t.pfn_lds);
+    row0 = __builtin_amdgcn_readfirstlane(t.pfn_row0);
+    nunits = __builtin_amdgcn_readfirstlane(t.pfn_nunits);
+    rows_total = __builtin_amdgcn_readfirstlane(t.pfn_rows_total);
+  }
+};
+
+template <int WFMT, int RPU>
+__device__ __forceinline__ void issue_prefetch_rpu(const VmParams& P, const PfNext& t, float* smem, int sw) {
+  using F = typename std::conditional<WFMT == AMK_W_BF16, FmtBf16,
+            typename std::conditional<WFMT == AMK_W_INT8_ROW, FmtInt8, FmtInt4>::type>::type;
+  const int lane = opaque_tid() & 63;
+  const int K = t.K, nunits = t.nunits, steps = t.steps;
+  const uint32_t rb = WFMT == AMK_W_BF16 ? (uint32_t)K * 2u : (WFMT == AMK_W_INT8_ROW ? (uint32_t)K : (uint32_t)K / 2u);
+  const uint32_t mb = WFMT == AMK_W_INT4_G128 ? (uint32_t)(K / 128) * 4u : 0u;
+  const uint8_t* tensor = P.wptr[t.tensor];
+  const uint8_t* data = tensor + (int64_t)t.row0 * rb;
+  const uint8_t* meta = tensor + (int64_t)t.rows_total * rb + (int64_t)t.row0 * mb;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(data, (uint32_t)nunits * RPU * rb);
+  const __amdgpu_buffer_rsrc_t rm = rsrc(meta, F::kMeta ? (uint32_t)nunits * RPU * mb : 0u);
+  const int nchunk = K / F::E, J = (nchunk + 63) >> 6;
+  const int jl = (nchunk - lane + 63) >> 6;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)t.lds);
+  constexpr uint32_t kStep = pf_row_step<F>();
+  for (int pass = 0; pass < 2; ++pass) {
+    const int v = pass == 0 ? sw : 0;  // own slabs, then a share of wave 0's
+    StepIter it;
+    it.init(v, nunits, J);
+    const int np = min(steps, it.n);
+    const uint32_t area = lds0 + (uint32_t)v * (uint32_t)steps * RPU * kStep;
+    for (int k = 0; k < np; ++k) {
+      if (v == sw || k % (kWaves - 1) == sw - 1) {
+        const bool valid = it.ij < jl;
+        const uint32_t off = (uint32_t)it.iu * RPU * rb + (uint32_t)(it.ij * 64 + lane) * 16u;
+        const uint32_t moff = (uint32_t)it.iu * RPU * mb + (uint32_t)(it.ij * 16 + (lane >> 2)) * 4u;
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) {
+          const uint32_t dst = area + (uint32_t)(k * RPU + r) * kStep;
+          dma16(rs, valid ? off + (uint32_t)r * rb : kOob, dst);
+          if constexpr (F::kMeta) dma4(rm, valid ? moff + (uint32_t)r * mb : kOob, dst + 1024u);
+        }
+      }
+      it.advance();
+    }
+  }
+}
+
+template <int WFMT>
+__device__ __forceinline__ void issue_prefetch(const VmParams& P, const PfNext& t, float* smem) {
+  if (t.steps <= 0) return;
+  const int sw = __builtin_amdgcn_readfirstlane(opaque_tid() >> 6);
+  if (sw == 0) return;
+  if (t.rpu == 2) issue_prefetch_rpu<WFMT, 2>(P, t, smem, sw);
+  else issue_prefetch_rpu<WFMT, 1>(P, t, smem, sw);
+}
+
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool run_one(const VmParams& P, const DevTask& t, float* smem) {
+__device__ __forceinline__ bool run_task(const VmParams& P, TaskRef t, float* smem) {
   switch (t.type) {
     case AMK_TASK_QKV: return task_qkv<DEPTH, WFMT>(P, t, smem);
     case AMK_TASK_ATTN: return task_attn(P, t, smem);
@@ -1016,6 +1180,15 @@ __device__ __forceinline__ bool run_one(const VmParams& P, const DevTask& t, flo
   }
 }
 
+template <int DEPTH, int WFMT>
+__device__ __forceinline__ bool run_one(const VmParams& P, TaskRef t, float* smem) {
+  const PfNext pf(t);
+  const bool ok = run_task<DEPTH, WFMT>(P, t, smem);
+  if (ok) issue_prefetch<WFMT>(P, pf, smem);
+  return ok;
+}
+
+
 // Workgroup b walks queue b in order.  A task that fails its wait (spin
 // budget spent, or another workgroup reported an error) ends the walk; the
 // error word tells every other workgroup to stop at its next wait.
@@ -1023,8 +1196,10 @@ template <int DEPTH, int WFMT>
 __global__ void __launch_bounds__(kThreads) amk_vm(VmParams P) {
   extern __shared__ __align__(16) float smem[];
   const int q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
-  for (int qi = q0; qi < q1; ++qi)
-    if (!run_one<DEPTH, WFMT>(P, P.tasks[P.queue[qi]], smem)) return;
+  for (int qi = q0; qi < q1; ++qi) {
+    const int ti = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)P.queue)[qi];
+    if (!run_one<DEPTH, WFMT>(P, ((CTask*)(uintptr_t)P.tasks)[ti], smem)) return;
+  }
 }
 
 // Plain streaming read of `bytes` (multiple of 16): grid-stride 16-byte
@@ -1141,6 +1316,28 @@ void free_engine(amk_engine* e) {
 
 // The kernel derives every address from (type, params) and the standard
 // buffer layout; refuse descriptions it cannot execute exactly as validated.
+// The weight rows a GEMV task streams (rpu = 0 for other task types); must
+// agree with the task functions of the kernel.
+struct GemvShape {
+  int32_t tensor = -1, rpu = 0;
+  int64_t row0 = 0, nunits = 0, K = 0, rows_total = 0;
+};
+GemvShape gemv_shape(const amk_model_config& m, const Task& t) {
+  const int64_t H = m.hidden, F = m.ffn, qd = (int64_t)m.n_heads * m.head_dim;
+  const int64_t qkv_rows = (int64_t)(m.n_heads + 2 * m.n_kv_heads) * m.head_dim;
+  GemvShape g;
+  const int32_t l = t.p[0];
+  switch (t.type) {
+    case AMK_TASK_QKV: g = {3 + 6 * l + LB_QKV, 2, 2 * (int64_t)t.p[1], (int64_t)t.p[2] - t.p[1], H, qkv_rows}; break;
+    case AMK_TASK_OPROJ: g = {3 + 6 * l + LB_O, 1, t.p[1], (int64_t)t.p[2] - t.p[1], qd, H}; break;
+    case AMK_TASK_GATEUP: g = {3 + 6 * l + LB_GATEUP, 2, 2 * (int64_t)t.p[1], (int64_t)t.p[2] - t.p[1], H, 2 * F}; break;
+    case AMK_TASK_DOWN: g = {3 + 6 * l + LB_DOWN, 1, t.p[1], (int64_t)t.p[2] - t.p[1], F, H}; break;
+    case AMK_TASK_LMHEAD: g = {2, 1, t.p[0], (int64_t)t.p[1] - t.p[0], H, m.vocab}; break;
+    default: break;
+  }
+  return g;
+}
+
 // output rows a projection task holds in LDS (0 for the other task types)
 int64_t task_res_rows(const Task& t) {
   switch (t.type) {
@@ -1160,6 +1357,8 @@ amk_status check_executable(const amk_schedule& s) {
     return fail(AMK_ERR_UNSUPPORTED, "schedule config is not in resolved form");
   if ((int64_t)s.queues.size() != s.config.num_cus)
     return fail(AMK_ERR_UNSUPPORTED, "queue count differs from num_cus");
+  if (3 + 6 * (int64_t)s.model.n_layers > 32767)
+    return fail(AMK_ERR_UNSUPPORTED, "too many layers for the device task record");
   const std::vector<Buffer> std_buffers = buffer_table(s.model, s.config.attn_splits);
   if (s.buffers.size() != std_buffers.size())
     return fail(AMK_ERR_UNSUPPORTED, "buffer table differs from the library layout");
@@ -1223,22 +1422,32 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     return code;
   };
 
-  // ---- LDS plan (floats)
-  const int64_t H = m.hidden, F = m.ffn, qd = (int64_t)m.n_heads * m.head_dim, hd = m.head_dim;
-  const int64_t kmax = std::max({H, F, qd});
+  // ---- LDS plan (floats).  Every task uses [0, lower(task)): the head, then
+  // a GEMV task's staged input and partial tables, or the attention scratch.
+  // Weight prefetch areas sit at the top of the workgroup's LDS.
+  const int64_t hd = m.head_dim;
   const int64_t E = m.wfmt == AMK_W_BF16 ? 8 : (m.wfmt == AMK_W_INT8_ROW ? 16 : 32);
-  const int64_t padded = (kmax + E * 64 - 1) / (E * 64) * (E * 64);
-  const int64_t xs_floats = padded + padded / 32;  // x + int4 chunk sums
-  int64_t res_rows = 1;
-  for (const Task& t : s->tasks) res_rows = std::max(res_rows, task_res_rows(t));
-  const int64_t res_floats = (res_rows + 3) / 4 * 4;
-  const int64_t tbl_floats = res_floats * kWaves;
+  auto xs_fl = [&](int64_t K) {
+    const int64_t padded = (K + E * 64 - 1) / (E * 64) * (E * 64);
+    return (padded + padded / 32 + 3) / 4 * 4;
+  };
   const int64_t att_floats = std::max<int64_t>(kWaves * 64 * 10 + 4 * (hd + 2), (int64_t)c.attn_splits * (hd + 1));
-  const int64_t head = 16;  // block-reduction slots + flag + int8 sum
-  const int64_t lds_x = head, lds_res = lds_x + xs_floats;
-  const int64_t lds_att = head;
-  const int64_t total_floats = std::max(lds_res + res_floats + tbl_floats, lds_att + att_floats);
-  e->lds_bytes = (size_t)total_floats * 4;
+  const int64_t lds_att = kHead;
+  auto lower = [&](const Task& t) -> int64_t {
+    const GemvShape g = gemv_shape(m, t);
+    if (g.rpu) return kHead + xs_fl(g.K) + (g.nunits * g.rpu + 3) / 4 * 4 * (1 + kWaves);
+    if (t.type == AMK_TASK_ATTN || t.type == AMK_TASK_MERGE) return lds_att + att_floats;
+    return kHead;
+  };
+  int64_t total_floats = kHead;
+  for (const Task& t : s->tasks) total_floats = std::max(total_floats, lower(t));
+  const bool prefetch = c.prefetch_kb > 0;
+  const int64_t lds_total = std::min<int64_t>((int64_t)prop.sharedMemPerBlock, 163840);
+  e->lds_bytes = prefetch ? (size_t)lds_total : (size_t)total_floats * 4;
+  if ((int64_t)total_floats * 4 > lds_total)
+    return (free_engine(e), fail(AMK_ERR_UNSUPPORTED, "schedule needs " + std::to_string(total_floats * 4) +
+                                                          " bytes of LDS per workgroup; device allows " +
+                                                          std::to_string(lds_total)));
   if (e->lds_bytes > (size_t)prop.sharedMemPerBlock)
     return (free_engine(e), fail(AMK_ERR_UNSUPPORTED, "schedule needs " + std::to_string(e->lds_bytes) +
                                                           " bytes of LDS per workgroup; device allows " +
@@ -1272,9 +1481,9 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     d.type = t.type;
     d.id = (int32_t)i;
     d.qslot = 0;
-    d.nwait = (int32_t)t.waits.size();
-    d.nsig = (int32_t)t.sigs.size();
-    std::copy(t.p, t.p + 8, d.p);
+    d.nwait = (int8_t)t.waits.size();
+    d.nsig = (int8_t)t.sigs.size();
+    std::copy(t.p, t.p + 6, d.p);
     for (size_t k = 0; k < t.waits.size(); ++k) {
       d.wctr[k] = t.waits[k].ctr;
       d.wthr[k] = t.waits[k].thr;
@@ -1285,6 +1494,36 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   }
   for (const auto& q : s->queues)
     for (size_t k = 0; k < q.size(); ++k) dt[q[k]].qslot = (int32_t)(k & 1);
+  // weight prefetch: the task before a GEMV task in its queue copies the
+  // GEMV's first slabs into LDS above everything either task uses, at most
+  // prefetch_kb, and at most ~56 DMA loads outstanding per issuing wave
+  if (prefetch)
+    for (const auto& q : s->queues)
+      for (size_t k = 1; k < q.size(); ++k) {
+        const Task& b = s->tasks[q[k]];
+        const GemvShape g = gemv_shape(m, b);
+        if (!g.rpu) continue;
+        const int64_t per_row = 1024 + (m.wfmt == AMK_W_INT4_G128 ? 256 : 0);
+        const int64_t step = g.rpu * per_row;
+        const int64_t used = 4 * std::max(lower(s->tasks[q[k - 1]]), lower(b));
+        const int64_t avail = std::min<int64_t>(lds_total - used - 64, (int64_t)c.prefetch_kb * 1024);
+        const int64_t dma_cap = 49 / (g.rpu * (m.wfmt == AMK_W_INT4_G128 ? 2 : 1));
+        const int64_t steps = std::min<int64_t>(avail / (kWaves * step), dma_cap);
+        if (steps < 1) continue;
+        const int64_t off = lds_total - kWaves * steps * step;
+        DevTask& d = dt[q[k]];
+        d.pf_have = (int8_t)steps;
+        d.pf_lds = (int32_t)off;
+        DevTask& a = dt[q[k - 1]];
+        a.pfn_tensor = (int16_t)g.tensor;
+        a.pfn_row0 = (int32_t)g.row0;
+        a.pfn_nunits = (int32_t)g.nunits;
+        a.pfn_rpu = (int8_t)g.rpu;
+        a.pfn_K = (int32_t)g.K;
+        a.pfn_steps = (int8_t)steps;
+        a.pfn_lds = (int32_t)off;
+        a.pfn_rows_total = (int32_t)g.rows_total;
+      }
   std::vector<int32_t> qoff(1, 0), queue;
   for (const auto& q : s->queues) {
     queue.insert(queue.end(), q.begin(), q.end());
@@ -1310,7 +1549,8 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
       (st = upload(e, &d_queue, queue)) != AMK_OK || (st = upload(e, &d_wptr, wptr)) != AMK_OK ||
       (st = upload(e, &d_rope, rope)) != AMK_OK)
     return bail(st);
-  const int64_t L = m.n_layers, S = c.attn_splits;
+  const int64_t L = m.n_layers, S = c.attn_splits, H = m.hidden, F = m.ffn;
+  const int64_t qd = (int64_t)m.n_heads * m.head_dim;
   if ((st = dev_alloc(e, &pr.x, (size_t)(L * 2 * H))) != AMK_OK ||
       (st = dev_alloc(e, &pr.q, (size_t)(L * qd))) != AMK_OK ||
       (st = dev_alloc(e, &pr.part, (size_t)(L * m.n_heads * S * (hd + 2)))) != AMK_OK ||
@@ -1338,10 +1578,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   pr.wfmt = m.wfmt;
   pr.act_bf16 = m.act_bf16;
   pr.eps = m.rms_eps;
-  pr.lds_x = (int32_t)lds_x;
-  pr.lds_res = (int32_t)lds_res;
   pr.lds_att = (int32_t)lds_att;
-  pr.res_floats = (int32_t)res_floats;
   pr.poll_late = c.poll_mode;
   pr.rel0 = c.release_mode;
   pr.spin_ticks = (uint64_t)2000000 * (uint64_t)e->wallclock_khz / 1000u;

@@ -95,3 +95,19 @@ def test_full_size_long_context(name, w8b):
     _free()
     agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
     log(f"{name} long: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+@pytest.mark.parametrize("sched", [{"prefetch_kb": -1}, {"prefetch_kb": 4}, {"poll_mode": 1},
+                                   {"release_mode": 1}, {"pipeline_depth": 4}, {"pipeline_depth": 16},
+                                   {"cu_policy": 1}, {"attn_splits": 3}],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_schedule_knobs_keep_parity(sched):
+    """Every ScheduleConfig knob the kernel reads, on the tiny decoder's full
+    protocol (ragged rows, several tiles per queue): same parity bar."""
+    wl = synth.get("tiny")
+    w = synth.model_weights(wl, seed=1)
+    toks = synth.tokens(2, wl.prompt_len + wl.decode_steps, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks, sched=sched)
+    del eng
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"tiny {sched}: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
