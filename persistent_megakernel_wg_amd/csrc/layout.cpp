@@ -53,10 +53,11 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   c.tiles_down = pick(c.tiles_down, c.num_cus);
   c.tiles_lm = pick(c.tiles_lm, c.num_cus);
   c.tiles_qkv = (int32_t)std::min<int64_t>(c.tiles_qkv, qkv_units);
-  c.tiles_o = std::min(c.tiles_o, m.hidden);
+  // O, down and LM-head tiles hold whole row pairs
+  c.tiles_o = std::min(c.tiles_o, std::max(1, m.hidden / 2));
   c.tiles_gateup = std::min(c.tiles_gateup, m.ffn);
-  c.tiles_down = std::min(c.tiles_down, m.hidden);
-  c.tiles_lm = std::min(c.tiles_lm, m.vocab);
+  c.tiles_down = std::min(c.tiles_down, std::max(1, m.hidden / 2));
+  c.tiles_lm = std::min(c.tiles_lm, std::max(1, m.vocab / 2));
   if (c.attn_splits <= 0) c.attn_splits = std::max(1, c.num_cus / m.n_kv_heads);
   if (c.attn_splits > 256) return fail(AMK_ERR_UNSUPPORTED, "attn_splits must be at most 256");
   if (c.cu_policy != 0 && c.cu_policy != 1) return fail(AMK_ERR_UNSUPPORTED, "cu_policy must be 0 or 1");

@@ -56,6 +56,10 @@ struct Builder {
 // bounds of piece i when n items are split into T nearly equal pieces
 inline int64_t split_at(int64_t n, int64_t T, int64_t i) { return (n * i) / T; }
 
+// the same with even bounds (rows go to the GEMV in pairs); an odd n leaves
+// the last piece one row longer
+inline int64_t split_even(int64_t n, int64_t T, int64_t i) { return i == T ? n : 2 * split_at(n / 2, T, i); }
+
 }  // namespace
 
 amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_schedule* s) {
@@ -89,7 +93,7 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
       b.add(AMK_TASK_MERGE, b.cu_of(h, nq), {l, h, S}, {{c_attn[h / grp], Pattn}}, {c_merge});
     for (int32_t i = 0; i < c.tiles_o; ++i)
       b.add(AMK_TASK_OPROJ, b.cu_of(i, c.tiles_o),
-            {l, (int32_t)split_at(m.hidden, c.tiles_o, i), (int32_t)split_at(m.hidden, c.tiles_o, i + 1)},
+            {l, (int32_t)split_even(m.hidden, c.tiles_o, i), (int32_t)split_even(m.hidden, c.tiles_o, i + 1)},
             {{c_merge, Pm}}, {c_o});
     for (int32_t i = 0; i < c.tiles_gateup; ++i)
       b.add(AMK_TASK_GATEUP, b.cu_of(i, c.tiles_gateup),
@@ -97,14 +101,14 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
             {{c_o, Po}}, {c_gu});
     for (int32_t i = 0; i < c.tiles_down; ++i)
       b.add(AMK_TASK_DOWN, b.cu_of(i, c.tiles_down),
-            {l, (int32_t)split_at(m.hidden, c.tiles_down, i), (int32_t)split_at(m.hidden, c.tiles_down, i + 1)},
+            {l, (int32_t)split_even(m.hidden, c.tiles_down, i), (int32_t)split_even(m.hidden, c.tiles_down, i + 1)},
             {{c_gu, Pg}}, {c_down});
     prev_down = c_down;
   }
   const int32_t c_lm = b.counter();
   for (int32_t i = 0; i < c.tiles_lm; ++i)
     b.add(AMK_TASK_LMHEAD, b.cu_of(i, c.tiles_lm),
-          {(int32_t)split_at(m.vocab, c.tiles_lm, i), (int32_t)split_at(m.vocab, c.tiles_lm, i + 1)},
+          {(int32_t)split_even(m.vocab, c.tiles_lm, i), (int32_t)split_even(m.vocab, c.tiles_lm, i + 1)},
           {{prev_down, Pd}}, {c_lm});
   s->queues.assign(c.num_cus, {});
   for (int32_t t = 0; t < (int32_t)s->tasks.size(); ++t) s->queues[s->tasks[t].cu].push_back(t);

@@ -729,7 +729,10 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* 
   const int H = P.H, qd = P.nq * P.hd;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
   const float* src = P.o + (int64_t)l * qd;
-  if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)) return false;
+  // rows go in pairs when the count is even (two loads per step), else singly
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)
+                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, qd, r0, (r1 - r0) / 2, src, nullptr);
+  if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(qd);
   float* dst = P.x + (int64_t)l * 2 * H;
   const int tid = opaque_tid();
@@ -774,7 +777,9 @@ __device__ __forceinline__ bool task_down(const VmParams& P, TaskRef t, float* s
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
   const float* src = P.a + (int64_t)l * F;
-  if (!project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)) return false;
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)
+                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, F, r0, (r1 - r0) / 2, src, nullptr);
+  if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(F);
   const float* mid = P.x + (int64_t)l * 2 * H;
   float* dst = P.x + ((int64_t)l * 2 + 1) * H;
@@ -793,7 +798,9 @@ __device__ __forceinline__ bool task_lmhead(const VmParams& P, TaskRef t, float*
   const uint8_t* w = P.wptr[2];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
   const float* src = P.x + ((int64_t)(P.L - 1) * 2 + 1) * H;
-  if (!project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)) return false;
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)
+                                : project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, P.V, H, r0, (r1 - r0) / 2, src, gain);
+  if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(H);
   for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
   vm_signal(P, t);
@@ -1334,6 +1341,11 @@ GemvShape gemv_shape(const amk_model_config& m, const Task& t) {
     case AMK_TASK_DOWN: g = {3 + 6 * l + LB_DOWN, 1, t.p[1], (int64_t)t.p[2] - t.p[1], F, H}; break;
     case AMK_TASK_LMHEAD: g = {2, 1, t.p[0], (int64_t)t.p[1] - t.p[0], H, m.vocab}; break;
     default: break;
+  }
+  // O, down and LM-head rows go in pairs when their count is even
+  if ((t.type == AMK_TASK_OPROJ || t.type == AMK_TASK_DOWN || t.type == AMK_TASK_LMHEAD) && g.nunits % 2 == 0) {
+    g.rpu = 2;
+    g.nunits /= 2;
   }
   return g;
 }
