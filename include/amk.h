@@ -89,6 +89,11 @@ typedef struct {
    *   release; 1: the epilogue stores and the release are issued by the
    *   polling wave alone while the others start the next task. */
   int32_t poll_mode, release_mode, prefetch_kb;
+  /* Relative work per XCD (permille; 0 = 1000): the GEMV rows of every phase
+   * are split over the queues in proportion to the weight of the XCD that
+   * runs each queue (queue c runs on XCD c % 8, the round-robin placement of
+   * workgroups over the 8 XCDs), to even out XCD speed differences. */
+  int32_t xcd_weight[8];
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */

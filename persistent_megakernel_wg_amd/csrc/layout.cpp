@@ -67,6 +67,11 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.poll_mode != 0 && c.poll_mode != 1) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0 or 1");
   if (c.release_mode != 0 && c.release_mode != 1)
     return fail(AMK_ERR_UNSUPPORTED, "release_mode must be 0 or 1");
+  for (int32_t x = 0; x < 8; ++x) {
+    if (c.xcd_weight[x] == 0) c.xcd_weight[x] = 1000;
+    if (c.xcd_weight[x] < 100 || c.xcd_weight[x] > 10000)
+      return fail(AMK_ERR_INVALID_ARG, "xcd_weight must be 0 (default) or 100..10000 permille");
+  }
   if (c.prefetch_kb == 0) c.prefetch_kb = 160;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");

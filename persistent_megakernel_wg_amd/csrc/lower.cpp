@@ -37,6 +37,23 @@ struct Builder {
     return (int32_t)((i * c.num_cus) / T);
   }
 
+  // bounds of T tiles over n items (in groups of `grain`), each tile's share
+  // proportional to the weight of the XCD its queue runs on
+  std::vector<int64_t> bounds(int64_t n, int64_t T, int64_t grain) const {
+    std::vector<int64_t> w(T), b(T + 1);
+    int64_t tot = 0;
+    for (int64_t i = 0; i < T; ++i) tot += (w[i] = c.xcd_weight[cu_of(i, T) % 8]);
+    const int64_t g = n / grain;  // whole groups; a remainder goes to the last tile
+    int64_t acc = 0;
+    for (int64_t i = 0; i <= T; ++i) {
+      b[i] = i == T ? n : grain * ((g * acc) / tot);
+      if (i < T) acc += w[i];
+    }
+    // at least one group per tile where possible
+    for (int64_t i = 1; i < T; ++i) b[i] = std::max(b[i], std::min(b[i - 1] + grain, n - grain * (T - i)));
+    return b;
+  }
+
   int32_t add(int32_t type, int32_t cu, std::initializer_list<int32_t> params,
               std::initializer_list<Wait> waits, std::initializer_list<int32_t> sigs) {
     Task t;
@@ -53,12 +70,6 @@ struct Builder {
   }
 };
 
-// bounds of piece i when n items are split into T nearly equal pieces
-inline int64_t split_at(int64_t n, int64_t T, int64_t i) { return (n * i) / T; }
-
-// the same with even bounds (rows go to the GEMV in pairs); an odd n leaves
-// the last piece one row longer
-inline int64_t split_even(int64_t n, int64_t T, int64_t i) { return i == T ? n : 2 * split_at(n / 2, T, i); }
 
 }  // namespace
 
@@ -79,8 +90,10 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
     std::vector<int32_t> c_attn(nkv);
     for (int32_t g = 0; g < nkv; ++g) c_attn[g] = b.counter();
     const int32_t c_merge = b.counter(), c_o = b.counter(), c_gu = b.counter(), c_down = b.counter();
+    const std::vector<int64_t> bq = b.bounds(U, c.tiles_qkv, 1), bo = b.bounds(m.hidden, c.tiles_o, 2),
+                               bg = b.bounds(m.ffn, c.tiles_gateup, 1), bd = b.bounds(m.hidden, c.tiles_down, 2);
     for (int32_t i = 0; i < c.tiles_qkv; ++i) {
-      const int32_t u0 = (int32_t)split_at(U, c.tiles_qkv, i), u1 = (int32_t)split_at(U, c.tiles_qkv, i + 1);
+      const int32_t u0 = (int32_t)bq[i], u1 = (int32_t)bq[i + 1];
       if (l == 0) b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {}, {c_qkv});
       else b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {{prev_down, Pd}}, {c_qkv});
     }
@@ -93,22 +106,22 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
       b.add(AMK_TASK_MERGE, b.cu_of(h, nq), {l, h, S}, {{c_attn[h / grp], Pattn}}, {c_merge});
     for (int32_t i = 0; i < c.tiles_o; ++i)
       b.add(AMK_TASK_OPROJ, b.cu_of(i, c.tiles_o),
-            {l, (int32_t)split_even(m.hidden, c.tiles_o, i), (int32_t)split_even(m.hidden, c.tiles_o, i + 1)},
+            {l, (int32_t)bo[i], (int32_t)bo[i + 1]},
             {{c_merge, Pm}}, {c_o});
     for (int32_t i = 0; i < c.tiles_gateup; ++i)
       b.add(AMK_TASK_GATEUP, b.cu_of(i, c.tiles_gateup),
-            {l, (int32_t)split_at(m.ffn, c.tiles_gateup, i), (int32_t)split_at(m.ffn, c.tiles_gateup, i + 1)},
+            {l, (int32_t)bg[i], (int32_t)bg[i + 1]},
             {{c_o, Po}}, {c_gu});
     for (int32_t i = 0; i < c.tiles_down; ++i)
       b.add(AMK_TASK_DOWN, b.cu_of(i, c.tiles_down),
-            {l, (int32_t)split_even(m.hidden, c.tiles_down, i), (int32_t)split_even(m.hidden, c.tiles_down, i + 1)},
+            {l, (int32_t)bd[i], (int32_t)bd[i + 1]},
             {{c_gu, Pg}}, {c_down});
     prev_down = c_down;
   }
   const int32_t c_lm = b.counter();
+  const std::vector<int64_t> bl = b.bounds(m.vocab, c.tiles_lm, 2);
   for (int32_t i = 0; i < c.tiles_lm; ++i)
-    b.add(AMK_TASK_LMHEAD, b.cu_of(i, c.tiles_lm),
-          {(int32_t)split_even(m.vocab, c.tiles_lm, i), (int32_t)split_even(m.vocab, c.tiles_lm, i + 1)},
+    b.add(AMK_TASK_LMHEAD, b.cu_of(i, c.tiles_lm), {(int32_t)bl[i], (int32_t)bl[i + 1]},
           {{prev_down, Pd}}, {c_lm});
   s->queues.assign(c.num_cus, {});
   for (int32_t t = 0; t < (int32_t)s->tasks.size(); ++t) s->queues[s->tasks[t].cu].push_back(t);

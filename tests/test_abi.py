@@ -179,3 +179,25 @@ def test_lowering_is_deterministic_and_safe_at_full_size():
         assert va["tasks"] == vb["tasks"] and va["queues"] == vb["queues"]
         a.close()
         b.close()
+
+
+def test_xcd_weights_shift_rows_and_stay_safe():
+    m = amk.ModelConfig.from_workload(synth.get("8b"))
+    c = amk.default_schedule_config(m, 256)
+    base = amk.Schedule.build(m, c).view()
+    for x in range(8):
+        c.xcd_weight[x] = 900 if x % 2 else 1100
+    sch = amk.Schedule.build(m, c)
+    assert sch.validate() == (0, -1, -1, -1)
+    v = sch.view()
+    for ty, lo, hi in ((5, 1, 2), (7, 0, 1)):  # gate/up units, LM-head rows
+        rows = {}
+        for t in v["tasks"]:
+            if t["type"] == ty and (ty == 7 or t["p"][0] == 0):
+                rows[t["cu"]] = t["p"][hi] - t["p"][lo]
+        even = np.mean([r for cu, r in rows.items() if cu % 2 == 0])
+        odd = np.mean([r for cu, r in rows.items() if cu % 2 == 1])
+        assert abs(even / odd - 1100 / 900) < 0.03, (ty, even, odd)
+    assert len(base["tasks"]) == len(v["tasks"])
+    c.xcd_weight[3] = 50
+    expect_status(amk.ERR_INVALID_ARG, amk.Schedule.build, m, c)
