@@ -94,6 +94,10 @@ typedef struct {
    * runs each queue (queue c runs on XCD c % 8, the round-robin placement of
    * workgroups over the 8 XCDs), to even out XCD speed differences. */
   int32_t xcd_weight[8];
+  /* Share (permille; 0 = default 1000) of an even O-projection tile given to
+   * queues that also run a MERGE task of the layer: those queues reach the
+   * O-projection late, so they get fewer of its rows. */
+  int32_t merge_o_share;
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */

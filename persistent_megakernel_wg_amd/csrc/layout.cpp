@@ -72,6 +72,9 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
     if (c.xcd_weight[x] < 100 || c.xcd_weight[x] > 10000)
       return fail(AMK_ERR_INVALID_ARG, "xcd_weight must be 0 (default) or 100..10000 permille");
   }
+  if (c.merge_o_share == 0) c.merge_o_share = 1000;
+  if (c.merge_o_share < 1 || c.merge_o_share > 1000)
+    return fail(AMK_ERR_INVALID_ARG, "merge_o_share must be 0 (default) or 1..1000 permille");
   if (c.prefetch_kb == 0) c.prefetch_kb = 160;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");

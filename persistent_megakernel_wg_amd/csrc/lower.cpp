@@ -39,10 +39,14 @@ struct Builder {
 
   // bounds of T tiles over n items (in groups of `grain`), each tile's share
   // proportional to the weight of the XCD its queue runs on
-  std::vector<int64_t> bounds(int64_t n, int64_t T, int64_t grain) const {
+  std::vector<int64_t> bounds(int64_t n, int64_t T, int64_t grain, const std::vector<char>* light = nullptr) const {
     std::vector<int64_t> w(T), b(T + 1);
     int64_t tot = 0;
-    for (int64_t i = 0; i < T; ++i) tot += (w[i] = c.xcd_weight[cu_of(i, T) % 8]);
+    for (int64_t i = 0; i < T; ++i) {
+      w[i] = c.xcd_weight[cu_of(i, T) % 8];
+      if (light && (*light)[cu_of(i, T)]) w[i] = w[i] * c.merge_o_share / 1000;
+      tot += w[i];
+    }
     const int64_t g = n / grain;  // whole groups; a remainder goes to the last tile
     int64_t acc = 0;
     for (int64_t i = 0; i <= T; ++i) {
@@ -90,7 +94,10 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
     std::vector<int32_t> c_attn(nkv);
     for (int32_t g = 0; g < nkv; ++g) c_attn[g] = b.counter();
     const int32_t c_merge = b.counter(), c_o = b.counter(), c_gu = b.counter(), c_down = b.counter();
-    const std::vector<int64_t> bq = b.bounds(U, c.tiles_qkv, 1), bo = b.bounds(m.hidden, c.tiles_o, 2),
+    // queues that run a MERGE task of the layer get a smaller O-projection tile
+    std::vector<char> merges(c.num_cus, 0);
+    for (int32_t h = 0; h < nq; ++h) merges[b.cu_of(h, nq)] = 1;
+    const std::vector<int64_t> bq = b.bounds(U, c.tiles_qkv, 1), bo = b.bounds(m.hidden, c.tiles_o, 2, &merges),
                                bg = b.bounds(m.ffn, c.tiles_gateup, 1), bd = b.bounds(m.hidden, c.tiles_down, 2);
     for (int32_t i = 0; i < c.tiles_qkv; ++i) {
       const int32_t u0 = (int32_t)bq[i], u1 = (int32_t)bq[i + 1];
