@@ -838,15 +838,22 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
     return p0 + ((blk * MAXC + c) * kAttnWaves + (wsc - 1)) * PW + pw;
   };
   auto koff = [&](int j, bool ok) { return ok ? (uint32_t)j * row_b + lane_off : kOob; };
-  u32x4 kr[MAXC], vr[MAXC];
-  if (wsc != 0) {
+  // two register buffers of blocks: blocks 0 and 1 are loaded before the
+  // wait (positions before pos only: rows of earlier launches); later blocks
+  // are loaded into the buffer just consumed, two blocks ahead
+  u32x4 ka[MAXC], va[MAXC], kb[MAXC], vb[MAXC];
+  auto load_blk = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk, bool before_wait) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const int j = posof(0, c);
-      const uint32_t o = koff(j, j < p1 && j < pos);
-      kr[c] = bload(rk, o);
-      vr[c] = bload(rv, o);
+      const int j = posof(blk, c);
+      const uint32_t o = koff(j, j < p1 && (!before_wait || j < pos));
+      k[c] = bload(rk, o);
+      v[c] = bload(rv, o);
     }
+  };
+  if (wsc != 0) {
+    load_blk(ka, va, 0, true);
+    load_blk(kb, vb, 1, true);
   }
   if (!vm_wait(P, t, flag)) return false;
   const bool hv = hh < nh;
@@ -865,23 +872,16 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
   const int len = p1 - p0;
   const int per_blk = MAXC * kAttnWaves * PW;
   const int nblk = wsc == 0 ? 0 : (len + per_blk - 1) / per_blk;
-  for (int blk = 0; blk < nblk; ++blk) {
-    if (blk > 0) {
+  // the row at pos (written by this launch) in a block loaded before the wait
+  auto patch_pos = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk) {
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int j = posof(blk, c);
-        const uint32_t o = koff(j, j < p1);
-        kr[c] = bload(rk, o);
-        vr[c] = bload(rv, o);
+    for (int c = 0; c < MAXC; ++c)
+      if (posof(blk, c) == pos) {
+        k[c] = bload(rk, koff(pos, true));
+        v[c] = bload(rv, koff(pos, true));
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c)
-        if (posof(0, c) == pos) {  // this launch's row, after the acquire
-          kr[c] = bload(rk, koff(pos, true));
-          vr[c] = bload(rv, koff(pos, true));
-        }
-    }
+  };
+  auto compute = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC], int blk) {
     float sc[MAXC];
     float bm = -INFINITY;
 #pragma unroll
@@ -919,6 +919,16 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
       acc[7] = fmaf(p, bf16_hi(v8.w), acc[7]);
     }
     M = nm;
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk == 0) patch_pos(ka, va, 0);
+    compute(ka, va, blk);
+    if (blk + 2 < nblk) load_blk(ka, va, blk + 2, false);
+    if (blk + 1 < nblk) {
+      if (blk == 0) patch_pos(kb, vb, 1);
+      compute(kb, vb, blk + 1);
+      if (blk + 3 < nblk) load_blk(kb, vb, blk + 3, false);
+    }
   }
   // merge the (wave, position group) states of each head through LDS
   float* wacc = smem + P.lds_att;         // [kWaves*64][8]
