@@ -58,7 +58,7 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   c.tiles_gateup = std::min(c.tiles_gateup, m.ffn);
   c.tiles_down = std::min(c.tiles_down, std::max(1, m.hidden / 2));
   c.tiles_lm = std::min(c.tiles_lm, std::max(1, m.vocab / 2));
-  if (c.attn_splits <= 0) c.attn_splits = std::max(1, c.num_cus / m.n_kv_heads);
+  if (c.attn_splits <= 0) c.attn_splits = std::max(1, 3 * c.num_cus / (4 * m.n_kv_heads));
   if (c.attn_splits > 256) return fail(AMK_ERR_UNSUPPORTED, "attn_splits must be at most 256");
   if (c.cu_policy != 0 && c.cu_policy != 1) return fail(AMK_ERR_UNSUPPORTED, "cu_policy must be 0 or 1");
   if (c.pipeline_depth == 0) c.pipeline_depth = 8;
@@ -75,7 +75,7 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.merge_o_share == 0) c.merge_o_share = 1000;
   if (c.merge_o_share < 1 || c.merge_o_share > 1000)
     return fail(AMK_ERR_INVALID_ARG, "merge_o_share must be 0 (default) or 1..1000 permille");
-  if (c.prefetch_kb == 0) c.prefetch_kb = 160;
+  if (c.prefetch_kb == 0) c.prefetch_kb = 64;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");
   if (c.fuse_flags == 0) c.fuse_flags = AMK_FUSE_DEFAULT;

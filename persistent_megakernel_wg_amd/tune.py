@@ -1,0 +1,176 @@
+"""Deterministic schedule tuner: the AutoMegaKernel summary's autoresearch
+loop ("Methodology", the autonomous research loop: propose a ScheduleConfig
+change, check it against a reference, measure latency, keep or revert)
+without the agent.  Candidates are proposed by coordinate descent over the
+knobs of ScheduleConfig in a fixed order; every candidate must
+
+  1. lower and pass the static safety gate (amk_validate; the engine refuses
+     unsafe schedules anyway),
+  2. reproduce the logits of the reference schedule (the library default,
+     the one the parity tests check against the oracle) within the parity
+     bar on a few decode steps,
+  3. be faster than the best so far by more than `min_gain` (median
+     kernel time over `steps` timed decode steps).
+
+Usage (one GPU):  python -m persistent_megakernel_wg_amd.tune --workload 8b --out best.json
+"""
+import argparse
+import json
+import sys
+import time
+
+import numpy as np
+
+# knob -> candidate values, tried in this order
+SPACE = [
+    ("attn_splits", [8, 16, 24, 32, 48]),
+    ("pipeline_depth", [4, 8, 16]),
+    ("prefetch_kb", [-1, 64, 96, 128, 160]),
+    ("poll_mode", [0, 1]),
+    ("cu_policy", [0, 1]),
+    ("release_mode", [0, 1]),
+]
+
+REL_L2 = 1e-2
+MAX_ABS = 2e-2
+
+
+def log(msg):
+    print(f"[tune] {msg}", file=sys.stderr, flush=True)
+
+
+def apply(cfg, overrides):
+    for k, v in overrides.items():
+        if isinstance(v, list):
+            arr = getattr(cfg, k)
+            for i, x in enumerate(v):
+                arr[i] = x
+        else:
+            setattr(cfg, k, v)
+    return cfg
+
+
+class Bench:
+    """Runs candidate schedules of one workload on shared device buffers."""
+
+    def __init__(self, wl, steps=32, warmup=8, check_steps=3):
+        import torch
+
+        import persistent_megakernel_wg_amd as amk
+        import synth
+        self.torch, self.amk = torch, amk
+        self.wl = wl
+        self.model = amk.ModelConfig.from_workload(wl)
+        self.cus = torch.cuda.get_device_properties(0).multi_processor_count
+        w = synth.model_weights(wl, seed=1)
+        self.dev_w = amk.upload_model(self.model, w)
+        del w
+        self.kv, self.logits = amk.alloc_state(self.model)
+        P = wl.prompt_len
+        self.P = P
+        self.kvp = torch.from_numpy(synth.kv_prefix(wl, P, seed=3).view(np.int16).reshape(-1)).to(self.kv.device)
+        self.toks = synth.tokens(2, P + warmup + steps + check_steps, wl.vocab)[P:]
+        self.steps, self.warmup, self.check_steps = steps, warmup, check_steps
+        self.reference = None
+
+    def config(self, overrides):
+        return apply(self.amk.default_schedule_config(self.model, self.cus), overrides)
+
+    def run(self, overrides):
+        """(median kernel ms, logits of the check steps) or raises."""
+        torch, amk = self.torch, self.amk
+        sched = amk.Schedule.build(self.model, self.config(overrides))
+        code = sched.validate()
+        if code[0] != 0:
+            raise RuntimeError(f"rejected by the safety gate: {code}")
+        eng = amk.Engine(sched, self.dev_w, self.kv, self.logits)
+        s = torch.cuda.current_stream()
+        try:
+            self.kv.copy_(self.kvp)
+            eng.set_kv_length(self.P)
+            out = []
+            for i in range(self.check_steps):
+                eng.decode_step(int(self.toks[i]), self.P + i, s)
+                torch.cuda.synchronize()
+                eng.check()
+                out.append(self.logits.cpu().numpy().astype(np.float64))
+            for i in range(self.warmup):
+                eng.decode_step(int(self.toks[i]), self.P + i, s)
+            e0 = [torch.cuda.Event(enable_timing=True) for _ in range(self.steps)]
+            e1 = [torch.cuda.Event(enable_timing=True) for _ in range(self.steps)]
+            for i in range(self.steps):
+                e0[i].record(s)
+                eng.decode_step(int(self.toks[i]), self.P + i, s)
+                e1[i].record(s)
+            torch.cuda.synchronize()
+            eng.check()
+            ms = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(self.steps)]))
+        finally:
+            eng.close()
+            sched.close()
+        return ms, out
+
+    def agrees(self, out):
+        for g, o in zip(out, self.reference):
+            rel = np.linalg.norm(g - o) / np.linalg.norm(o)
+            mab = np.max(np.abs(g - o)) / np.max(np.abs(o))
+            if rel > REL_L2 or mab > MAX_ABS:
+                return False, rel
+        return True, 0.0
+
+
+def tune(wl, min_gain=0.005, steps=48, space=SPACE):
+    b = Bench(wl, steps=steps)
+    default = b.config({})
+    best = {}
+    best_ms, b.reference = b.run(best)
+    log(f"reference (library default) {best_ms:.4f} ms")
+    history = [{"overrides": {}, "ms": best_ms, "kept": True}]
+    for knob, values in space:
+        for v in values:
+            cand = dict(best)
+            cand[knob] = v
+            current = best.get(knob, getattr(default, knob))
+            if v == current:
+                continue
+            try:
+                ms, out = b.run(cand)
+            except Exception as e:  # unsafe or unsupported: reverted
+                history.append({"overrides": cand, "error": str(e), "kept": False})
+                log(f"{cand}: {e}")
+                continue
+            ok, rel = b.agrees(out)
+            kept = ok and ms < best_ms * (1 - min_gain)
+            history.append({"overrides": cand, "ms": ms, "parity": ok, "kept": kept})
+            log(f"{cand}: {ms:.4f} ms parity {'ok' if ok else 'FAIL %.2e' % rel}{' KEEP' if kept else ''}")
+            if kept:
+                best, best_ms = cand, ms
+    # re-measure the winner against the reference, interleaved
+    ref, win = [], []
+    for _ in range(2):
+        ref.append(b.run({})[0])
+        win.append(b.run(best)[0])
+    return {"workload": wl.name, "best": best, "ms": float(np.median(win)), "reference_ms": float(np.median(ref)),
+            "history": history}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="8b")
+    ap.add_argument("--out", default="")
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--min-gain", type=float, default=0.005)
+    args = ap.parse_args()
+    import synth
+    t0 = time.time()
+    res = tune(synth.get(args.workload), args.min_gain, args.steps)
+    res["seconds"] = time.time() - t0
+    text = json.dumps(res, indent=1)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(json.dumps({k: res[k] for k in ("workload", "best", "ms", "reference_ms", "seconds")}))
+
+
+if __name__ == "__main__":
+    main()

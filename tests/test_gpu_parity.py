@@ -111,3 +111,15 @@ def test_schedule_knobs_keep_parity(sched):
     del eng
     agree, rel, mab = check_run(res, min_argmax=1.0)
     log(f"tiny {sched}: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+def test_tuner_keeps_only_safe_agreeing_faster_configs():
+    """The schedule tuner on the tiny decoder with a two-knob space: every kept
+    step passed the gate and reproduced the reference logits."""
+    from persistent_megakernel_wg_amd import tune
+    res = tune.tune(synth.get("tiny"), steps=8, space=[("attn_splits", [1, 2]), ("pipeline_depth", [4, 16])])
+    assert res["history"][0]["kept"]
+    for h in res["history"][1:]:
+        if h.get("kept"):
+            assert h["parity"] and "error" not in h
+    log(f"tuner tiny: best {res['best']} {res['ms']:.4f} ms vs {res['reference_ms']:.4f} ms")
