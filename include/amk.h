@@ -102,6 +102,17 @@ typedef struct {
    * queues that also run a MERGE task of the layer: those queues reach the
    * O-projection late, so they get fewer of its rows. */
   int32_t merge_o_share;
+  /* merge_place 0: MERGE tasks spread over the queues that run no attention
+   * split of the layer (when there are such queues); 1: spread over all
+   * queues like the other phases. */
+  int32_t merge_place;
+  /* LDS kilobytes prefetched for a GEMV task whose queue runs attention work
+   * (ATTN or MERGE tasks) just before it: the O-projection.  HBM is mostly
+   * idle during attention, so the default (0) takes all that fits; -1 uses
+   * prefetch_kb (and is off when that is off); otherwise 1..1024.  A MERGE task between the two is
+   * skipped: the task before it issues the copy, so that the merge does not
+   * wait behind it. */
+  int32_t prefetch_attn_kb;
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */

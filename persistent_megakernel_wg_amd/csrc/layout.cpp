@@ -75,9 +75,15 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.merge_o_share == 0) c.merge_o_share = 1000;
   if (c.merge_o_share < 1 || c.merge_o_share > 1000)
     return fail(AMK_ERR_INVALID_ARG, "merge_o_share must be 0 (default) or 1..1000 permille");
+  if (c.merge_place != 0 && c.merge_place != 1) return fail(AMK_ERR_UNSUPPORTED, "merge_place must be 0 or 1");
   if (c.prefetch_kb == 0) c.prefetch_kb = 64;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");
+  // resolved: -1 = off, else a budget in KB
+  if (c.prefetch_attn_kb == -1) c.prefetch_attn_kb = c.prefetch_kb;
+  if (c.prefetch_attn_kb == 0) c.prefetch_attn_kb = 1024;
+  if (c.prefetch_attn_kb != -1 && (c.prefetch_attn_kb < 1 || c.prefetch_attn_kb > 1024))
+    return fail(AMK_ERR_INVALID_ARG, "prefetch_attn_kb must be -1 (as prefetch_kb), 0 (all that fits) or 1..1024");
   if (c.fuse_flags == 0) c.fuse_flags = AMK_FUSE_DEFAULT;
   if (c.fuse_flags != AMK_FUSE_DEFAULT)
     return fail(AMK_ERR_UNSUPPORTED, "only the fully fused task set (AMK_FUSE_DEFAULT) is built");

@@ -94,9 +94,22 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
     std::vector<int32_t> c_attn(nkv);
     for (int32_t g = 0; g < nkv; ++g) c_attn[g] = b.counter();
     const int32_t c_merge = b.counter(), c_o = b.counter(), c_gu = b.counter(), c_down = b.counter();
-    // queues that run a MERGE task of the layer get a smaller O-projection tile
+    // MERGE queues: by default spread over the queues that run no attention
+    // split (a merge queue then holds no attention loads when the splits of
+    // its head land); queues that run a MERGE task of the layer get a
+    // smaller O-projection tile
+    const int64_t n_attn = (int64_t)nkv * S;
+    std::vector<char> attn_q(c.num_cus, 0);
+    for (int64_t i = 0; i < n_attn; ++i) attn_q[b.cu_of(i, n_attn)] = 1;
+    std::vector<int32_t> free_q;
+    for (int32_t q = 0; q < c.num_cus; ++q)
+      if (!attn_q[q]) free_q.push_back(q);
+    const bool spread_free = c.merge_place == 0 && !free_q.empty();
+    auto merge_cu = [&](int32_t h) {
+      return spread_free ? free_q[(size_t)(((int64_t)h * (int64_t)free_q.size()) / nq)] : b.cu_of(h, nq);
+    };
     std::vector<char> merges(c.num_cus, 0);
-    for (int32_t h = 0; h < nq; ++h) merges[b.cu_of(h, nq)] = 1;
+    for (int32_t h = 0; h < nq; ++h) merges[merge_cu(h)] = 1;
     const std::vector<int64_t> bq = b.bounds(U, c.tiles_qkv, 1), bo = b.bounds(m.hidden, c.tiles_o, 2, &merges),
                                bg = b.bounds(m.ffn, c.tiles_gateup, 1), bd = b.bounds(m.hidden, c.tiles_down, 2);
     for (int32_t i = 0; i < c.tiles_qkv; ++i) {
@@ -104,13 +117,12 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
       if (l == 0) b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {}, {c_qkv});
       else b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {{prev_down, Pd}}, {c_qkv});
     }
-    const int64_t n_attn = (int64_t)nkv * S;
     for (int32_t g = 0; g < nkv; ++g)
       for (int32_t sp = 0; sp < S; ++sp)
         b.add(AMK_TASK_ATTN, b.cu_of((int64_t)g * S + sp, n_attn), {l, g, sp, S}, {{c_qkv, Pq}},
               {c_attn[g]});
     for (int32_t h = 0; h < nq; ++h)
-      b.add(AMK_TASK_MERGE, b.cu_of(h, nq), {l, h, S}, {{c_attn[h / grp], Pattn}}, {c_merge});
+      b.add(AMK_TASK_MERGE, merge_cu(h), {l, h, S}, {{c_attn[h / grp], Pattn}}, {c_merge});
     for (int32_t i = 0; i < c.tiles_o; ++i)
       b.add(AMK_TASK_OPROJ, b.cu_of(i, c.tiles_o),
             {l, (int32_t)bo[i], (int32_t)bo[i + 1]},

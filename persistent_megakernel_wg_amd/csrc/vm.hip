@@ -1463,7 +1463,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   };
   int64_t total_floats = kHead;
   for (const Task& t : s->tasks) total_floats = std::max(total_floats, lower(t));
-  const bool prefetch = c.prefetch_kb > 0;
+  const bool prefetch = c.prefetch_kb > 0 || c.prefetch_attn_kb > 0;
   const int64_t lds_total = std::min<int64_t>((int64_t)prop.sharedMemPerBlock, 163840);
   e->lds_bytes = prefetch ? (size_t)lds_total : (size_t)total_floats * 4;
   if ((int64_t)total_floats * 4 > lds_total)
@@ -1517,18 +1517,28 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   for (const auto& q : s->queues)
     for (size_t k = 0; k < q.size(); ++k) dt[q[k]].qslot = (int32_t)(k & 1);
   // weight prefetch: the task before a GEMV task in its queue copies the
-  // GEMV's first slabs into LDS above everything either task uses, at most
-  // prefetch_kb, and at most ~56 DMA loads outstanding per issuing wave
+  // GEMV's first slabs into LDS above everything the tasks from the issuer
+  // to the GEMV use, and at most ~56 DMA loads outstanding per issuing wave.
+  // MERGE tasks are stepped over (the task before them issues the copy, so
+  // a merge's loads do not queue behind it); the budget is prefetch_attn_kb
+  // when attention work precedes the GEMV in its queue, else prefetch_kb.
   if (prefetch)
     for (const auto& q : s->queues)
       for (size_t k = 1; k < q.size(); ++k) {
         const Task& b = s->tasks[q[k]];
         const GemvShape g = gemv_shape(m, b);
         if (!g.rpu) continue;
+        size_t j = k - 1;
+        int64_t used_f = lower(b);
+        while (j > 0 && s->tasks[q[j]].type == AMK_TASK_MERGE) used_f = std::max(used_f, lower(s->tasks[q[j--]]));
+        used_f = std::max(used_f, lower(s->tasks[q[j]]));
+        const int32_t prev_ty = s->tasks[q[k - 1]].type;
+        const int32_t kb = prev_ty == AMK_TASK_ATTN || prev_ty == AMK_TASK_MERGE ? c.prefetch_attn_kb : c.prefetch_kb;
+        if (kb <= 0) continue;
         const int64_t per_row = 1024 + (m.wfmt == AMK_W_INT4_G128 ? 256 : 0);
         const int64_t step = g.rpu * per_row;
-        const int64_t used = 4 * std::max(lower(s->tasks[q[k - 1]]), lower(b));
-        const int64_t avail = std::min<int64_t>(lds_total - used - 64, (int64_t)c.prefetch_kb * 1024);
+        const int64_t used = 4 * used_f;
+        const int64_t avail = std::min<int64_t>(lds_total - used - 64, (int64_t)kb * 1024);
         const int64_t dma_cap = 49 / (g.rpu * (m.wfmt == AMK_W_INT4_G128 ? 2 : 1));
         const int64_t steps = std::min<int64_t>(avail / (kWaves * step), dma_cap);
         if (steps < 1) continue;
@@ -1536,7 +1546,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
         DevTask& d = dt[q[k]];
         d.pf_have = (int8_t)steps;
         d.pf_lds = (int32_t)off;
-        DevTask& a = dt[q[k - 1]];
+        DevTask& a = dt[q[j]];
         a.pfn_tensor = (int16_t)g.tensor;
         a.pfn_row0 = (int32_t)g.row0;
         a.pfn_nunits = (int32_t)g.nunits;

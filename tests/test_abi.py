@@ -201,3 +201,25 @@ def test_xcd_weights_shift_rows_and_stay_safe():
     assert len(base["tasks"]) == len(v["tasks"])
     c.xcd_weight[3] = 50
     expect_status(amk.ERR_INVALID_ARG, amk.Schedule.build, m, c)
+
+
+def test_merge_tasks_avoid_attention_queues():
+    m = amk.ModelConfig.from_workload(synth.get("8b"))
+    for place, disjoint in ((0, True), (1, False)):
+        c = amk.default_schedule_config(m, 256)
+        c.merge_place = place
+        s = amk.Schedule.build(m, c)
+        assert s.validate() == (0, -1, -1, -1)
+        v = s.view()
+        for layer in (0, 31):
+            att = {t["cu"] for t in v["tasks"] if t["type"] == 2 and t["p"][0] == layer}
+            mer = [t["cu"] for t in v["tasks"] if t["type"] == 3 and t["p"][0] == layer]
+            assert len(mer) == m.n_heads and len(set(mer)) == m.n_heads
+            assert (not (att & set(mer))) == disjoint
+        s.close()
+    c = amk.default_schedule_config(m, 256)
+    c.merge_place = 2
+    expect_status(amk.ERR_UNSUPPORTED, amk.Schedule.build, m, c)
+    c = amk.default_schedule_config(m, 256)
+    c.prefetch_attn_kb = -2
+    expect_status(amk.ERR_INVALID_ARG, amk.Schedule.build, m, c)
