@@ -113,6 +113,20 @@ typedef struct {
    * skipped: the task before it issues the copy, so that the merge does not
    * wait behind it. */
   int32_t prefetch_attn_kb;
+  /* How a task learns that its inputs are written (the dependency edges of
+   * the schedule stay the same):
+   * 0: counters.  A producer waits for its stores, then adds 1 to each
+   *    counter it signals; a consumer polls its counters, then reads.
+   * 1: tagged activations.  Every value one task hands to another is stored
+   *    as a 64-bit word {float, launch tag} in one single-copy-atomic store;
+   *    a consumer reads the words it needs and re-reads those that do not
+   *    yet carry this launch's tag.  No counter traffic, and the read is the
+   *    wait.
+   * 2: as 1, except the FFN activation (gate/up -> down, ffn values read in
+   *    full by every down task): it keeps the counter, so that those reads
+   *    move 4 bytes per value instead of 8.
+   * 1 and 2 need attn_splits <= 512 and attn_splits * head_dim <= 8192. */
+  int32_t sync_mode;
 } amk_schedule_config;
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */
@@ -230,7 +244,10 @@ typedef struct {
 /* ---- configuration ------------------------------------------------------ */
 
 /* Default ScheduleConfig for a model on a device with device_cus compute
- * units (one queue per CU). */
+ * units (one queue per CU): every field resolved; sync_mode 1 where the
+ * attention split count allows it, else 0.  (A zero-filled config passed to
+ * amk_build_schedule resolves the same way except that its sync_mode 0
+ * stays the counter protocol.) */
 amk_status amk_default_schedule_config(const amk_model_config* model, int32_t device_cus,
                                        amk_schedule_config* out);
 

@@ -76,6 +76,9 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.merge_o_share < 1 || c.merge_o_share > 1000)
     return fail(AMK_ERR_INVALID_ARG, "merge_o_share must be 0 (default) or 1..1000 permille");
   if (c.merge_place != 0 && c.merge_place != 1) return fail(AMK_ERR_UNSUPPORTED, "merge_place must be 0 or 1");
+  if (c.sync_mode < 0 || c.sync_mode > 2) return fail(AMK_ERR_UNSUPPORTED, "sync_mode must be 0, 1 or 2");
+  if (c.sync_mode != 0 && (c.attn_splits > 512 || (int64_t)c.attn_splits * m.head_dim > 8192))
+    return fail(AMK_ERR_UNSUPPORTED, "sync_mode 1 and 2 need attn_splits <= 512 and attn_splits * head_dim <= 8192");
   if (c.prefetch_kb == 0) c.prefetch_kb = 64;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");

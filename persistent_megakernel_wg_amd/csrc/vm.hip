@@ -71,6 +71,18 @@ struct VmParams {
   // queue-walk knobs of the schedule configuration
   int32_t poll_late;  // the polling wave issues its weight prologue after the wait
   int32_t rel0;       // epilogue stores and release by wave 0 alone
+  // tagged activations (sync_mode 1): every value one task hands to another
+  // is a 64-bit word {float bits, launch tag}; a reader spins on the words
+  // it needs instead of on counters, a writer only stores
+  int32_t tagged;
+  int32_t a_tagged;  // the FFN activation (gate/up -> down) is tagged too; else that edge keeps its counter
+  uint32_t tag;
+  uint64_t* tx;    // [L][2][H] as x
+  uint64_t* tq;    // [L][nq*hd] as q
+  uint64_t* tkv;   // [L][2][nkv*hd] K (roped) and V of this launch's position, bf16 values
+  uint64_t* tpart; // [L][nq][S][hd+2] as part
+  uint64_t* to;    // [L][nq*hd] as o
+  uint64_t* ta;    // [L][F] as a
 };
 
 // ------------------------------------------------------------- helpers --
@@ -168,6 +180,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// true in every thread when `pred` holds in any thread; `red` holds kWaves
+// floats of LDS
+__device__ __forceinline__ bool block_any(bool pred, float* red) {
+  const bool w = __builtin_amdgcn_ballot_w64(pred) != 0;
+  if ((opaque_tid() & 63) == 0) reinterpret_cast<int*>(red)[opaque_tid() >> 6] = w ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) any |= reinterpret_cast<const int*>(red)[k];
+  __syncthreads();
+  return any != 0;
+}
+
 // relaxed agent-scope load: a vector load that no cache level keeps stale
 // across the acquire done by the waiting thread
 __device__ __forceinline__ float ld_agent(const float* p) {
@@ -184,6 +209,20 @@ __device__ __forceinline__ void st_agent(float* p, float v) {
 __device__ __forceinline__ void st_agent(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Tagged words: the value in the low half, the launch's tag in the high half,
+// written and read as one aligned 64-bit agent-scope access (single-copy
+// atomic), so a word that carries this launch's tag carries this launch's
+// value.  Stores go through to the device coherence point; a reader's
+// agent-scope loads see them without any fence.
+__device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // Buffer descriptor over [base, base + bytes).  Base and size are the same in
 // every lane; reading them through readfirstlane lets the compiler keep the
@@ -213,6 +252,12 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // the next task cannot overwrite a flag a slower wave has yet to read.
 template <typename Hook>
 __device__ __forceinline__ bool vm_wait(const VmParams& P, TaskRef t, int* flags, Hook&& before_barrier) {
+  if (P.tagged && (P.a_tagged || t.type != AMK_TASK_DOWN)) {  // the task's reads of tagged words are its wait
+    if (P.trace && opaque_tid() == 0) P.trace[(size_t)t.id * 4 + 0] = wall_clock64();
+    before_barrier();
+    __syncthreads();
+    return true;
+  }
   int* flag = flags + t.qslot;
   if (opaque_tid() == 0) {
     if (P.trace) P.trace[(size_t)t.id * 4 + 0] = wall_clock64();
@@ -247,6 +292,57 @@ __device__ __forceinline__ bool vm_wait(const VmParams& P, TaskRef t, int* flags
   return vm_wait(P, t, flags, [] {});
 }
 
+// Spin state of one thread's tagged reads.  again() is called while some
+// word lacks the launch's tag: it backs off, and gives up (reporting the
+// error to every workgroup) when the spin budget is spent or another
+// workgroup already reported one.
+struct TagSpin {
+  uint64_t start = 0;
+  uint32_t polls = 0;
+  bool failed = false;
+  __device__ __forceinline__ bool again(const VmParams& P) {
+    if (start == 0) start = wall_clock64();
+    __builtin_amdgcn_s_sleep(1);
+    // every re-read is a memory round trip, so the clock is checked each time
+    if (wall_clock64() - start > P.spin_ticks ||
+        ((++polls & 15u) == 0u && __hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)) {
+      __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      failed = true;
+      return false;
+    }
+    return true;
+  }
+};
+
+// The tagged words p[idx(k)] for the k < N with use(k): issued together, then
+// re-read until each carries the launch's tag.  v[k] = the value (0 where
+// !use(k)).  False when the spin gave up.
+template <int N, class Use, class Idx>
+__device__ __forceinline__ bool ld_tagged(const VmParams& P, const uint64_t* p, Use&& use, Idx&& idx,
+                                          float (&v)[N], TagSpin& sp) {
+  const uint64_t ok = (uint64_t)P.tag << 32;
+  uint64_t w[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) w[k] = use(k) ? ld_tag(p + idx(k)) : ok;
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) all = all && (w[k] >> 32) == (ok >> 32);
+    if (all) break;
+    if (!sp.again(P)) return false;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((w[k] >> 32) != (ok >> 32)) w[k] = ld_tag(p + idx(k));
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = tag_val(w[k]);
+  return true;
+}
+
+__device__ __forceinline__ void trace_mark(const VmParams& P, TaskRef t, int k) {
+  if (P.trace && opaque_tid() == 0) P.trace[(size_t)t.id * 4 + k] = wall_clock64();
+}
+
 // Release.  Every store another workgroup reads is a write-through
 // agent-scope store, so its completion (vmcnt) means it is visible at the
 // device coherence point; lane 0 of wave 0 then bumps each counter with a
@@ -258,6 +354,14 @@ __device__ __forceinline__ int epilogue_threads(const VmParams& P) { return P.re
 
 __device__ __forceinline__ void vm_signal(const VmParams& P, TaskRef t) {
   const int tid = opaque_tid();
+  if (P.tagged && (P.a_tagged || t.type != AMK_TASK_GATEUP)) {  // the stores were the signal
+    if (P.trace && tid == 0) {
+      const uint64_t now = wall_clock64();
+      P.trace[(size_t)t.id * 4 + 2] = now;
+      P.trace[(size_t)t.id * 4 + 3] = now;
+    }
+    return;
+  }
   if (!P.rel0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -398,14 +502,36 @@ struct FmtInt4 {
   }
 };
 
-// x (fp32 or bf16 source) -> optional RMSNorm with bf16 gain -> optional bf16
-// rounding -> LDS in the chunk layout of format F; int8 also gets sum x,
-// int4 the per-chunk sums of x.  n is a multiple of 8.
+// x (fp32 or bf16 source, or tagged words when tsrc is set) -> optional
+// RMSNorm with bf16 gain -> optional bf16 rounding -> LDS in the chunk
+// layout of format F; int8 also gets sum x, int4 the per-chunk sums of x.
+// n is a multiple of 8.  False when a tagged read gave up.
 template <class F, bool SRC_BF16, bool NORM>
-__device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* gain, float eps,
-                                        int act_bf16, float* xs, float* red, float* xsum, float* csum) {
+__device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, const uint64_t* tsrc, int n,
+                                        const uint16_t* gain, float* xs, float* red, float* xsum, float* csum) {
   const int tid = opaque_tid(), n4 = n >> 2;
+  const float eps = P.eps;
+  const int act_bf16 = P.act_bf16;
   float ss = 0.0f;
+  if (tsrc) {  // up to 4 groups of 4 words per thread in flight at once
+    TagSpin sp;
+    for (int i0 = tid; i0 < n4; i0 += kThreads * 4) {
+      float v[16];
+      if (!ld_tagged<16>(P, tsrc, [&](int k) { return i0 + (k >> 2) * kThreads < n4; },
+                         [&](int k) { return 4 * (i0 + (k >> 2) * kThreads) + (k & 3); }, v, sp))
+        break;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = i0 + g * kThreads;
+        if (i < n4) {
+          const float4 f = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+          if (NORM) ss += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+          *reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4)) = f;
+        }
+      }
+    }
+    if (block_any(sp.failed, red)) return false;
+  } else
   for (int i = tid; i < n4; i += kThreads) {
     float4 v;
     if (SRC_BF16) {
@@ -455,6 +581,7 @@ __device__ __forceinline__ void stage_x(const void* src, int n, const uint16_t* 
     }
     __syncthreads();
   }
+  return true;
 }
 
 // Issue order of one wave's steps: its round units (sw, sw + 8, ...) slab by
@@ -635,7 +762,7 @@ __device__ __forceinline__ int xs_floats(int K) {
 template <int DEPTH, int WFMT, int RPU, bool SRC_BF16, bool NORM>
 __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* smem, const uint8_t* ptr,
                                         int64_t rows_total, int K, int row0, int nunits, const void* src,
-                                        const uint16_t* gain) {
+                                        const uint64_t* tsrc, const uint16_t* gain) {
   using F = typename std::conditional<WFMT == AMK_W_BF16, FmtBf16,
             typename std::conditional<WFMT == AMK_W_INT8_ROW, FmtInt8, FmtInt4>::type>::type;
   float* red = smem;                                  // kWaves floats
@@ -662,7 +789,8 @@ __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* sme
     ok = vm_wait(P, t, flag, [&] {
       if (pf_wait) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
     });
-    if (ok) stage_x<F, SRC_BF16, NORM>(src, K, gain, P.eps, P.act_bf16, xs, red, xsum, csum);
+    if (ok) ok = stage_x<F, SRC_BF16, NORM>(P, src, tsrc, K, gain, xs, red, xsum, csum);
+    if (ok && P.tagged) trace_mark(P, t, 1);
   });
   if (!ok) return false;
   const int J = (K / F::E + 63) >> 6;
@@ -689,10 +817,11 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, TaskRef t, float* sm
   bool ok;
   if (l == 0) {
     const void* src = P.wptr[0] + (int64_t)P.token * H * 2;
-    ok = project<DEPTH, WFMT, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+    ok = project<DEPTH, WFMT, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, nullptr, gain);
   } else {
-    const void* src = P.x + ((int64_t)(l - 1) * 2 + 1) * H;
-    ok = project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, gain);
+    const int64_t off = ((int64_t)(l - 1) * 2 + 1) * H;
+    ok = project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, P.x + off,
+                                              P.tagged ? P.tx + off : nullptr, gain);
   }
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(H);
@@ -709,14 +838,25 @@ __device__ __forceinline__ bool task_qkv(const VmParams& P, TaskRef t, float* sm
       b = rb;
     }
     if (hs < nq) {
-      float* qd = P.q + (int64_t)l * nq * hd + (int64_t)hs * hd;
-      st_agent(qd + i, a);
-      st_agent(qd + i + half, b);
+      const int64_t qo = (int64_t)l * nq * hd + (int64_t)hs * hd;
+      if (P.tagged) {
+        st_tag(P.tq + qo + i, a, P.tag);
+        st_tag(P.tq + qo + i + half, b, P.tag);
+      } else {
+        st_agent(P.q + qo + i, a);
+        st_agent(P.q + qo + i + half, b);
+      }
     } else {
       const int kvsel = hs < nq + nkv ? 0 : 1, g = hs - nq - kvsel * nkv;
       uint16_t* row = P.kv + ((((int64_t)l * 2 + kvsel) * nkv + g) * P.mc + P.pos) * hd;
-      st_agent(row + i, (uint16_t)bf16_bits(a));
-      st_agent(row + i + half, (uint16_t)bf16_bits(b));
+      const uint32_t ba = bf16_bits(a), bb = bf16_bits(b);
+      st_agent(row + i, (uint16_t)ba);
+      st_agent(row + i + half, (uint16_t)bb);
+      if (P.tagged) {  // this launch's row for the attention tasks, as tagged bf16 values
+        uint64_t* tr = P.tkv + (((int64_t)l * 2 + kvsel) * nkv + g) * hd;
+        st_tag(tr + i, __uint_as_float(ba << 16), P.tag);
+        st_tag(tr + i + half, __uint_as_float(bb << 16), P.tag);
+      }
     }
   }
   vm_signal(P, t);
@@ -729,21 +869,32 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* 
   const int H = P.H, qd = P.nq * P.hd;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
   const float* src = P.o + (int64_t)l * qd;
+  const uint64_t* tsrc = P.tagged ? P.to + (int64_t)l * qd : nullptr;
   // rows go in pairs when the count is even (two loads per step), else singly
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, nullptr)
-                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, qd, r0, (r1 - r0) / 2, src, nullptr);
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, tsrc, nullptr)
+                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, qd, r0, (r1 - r0) / 2, src, tsrc, nullptr);
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(qd);
-  float* dst = P.x + (int64_t)l * 2 * H;
+  const int64_t dst = (int64_t)l * 2 * H, prev = ((int64_t)(l - 1) * 2 + 1) * H;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
-  if (tid < EW)
+  if (P.tagged) {  // residual rows of the previous layer's output are tagged words too
+    TagSpin sp;
+    for (int k = tid; k < r1 - r0 && !sp.failed; k += kThreads) {
+      const int r = r0 + k;
+      float resid[1];
+      if (l == 0) resid[0] = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
+      else if (!ld_tagged<1>(P, P.tx + prev, [](int) { return true; }, [&](int) { return r; }, resid, sp)) break;
+      st_tag(P.tx + dst + r, resid[0] + res[k], P.tag);
+    }
+    if (block_any(sp.failed, smem)) return false;
+  } else if (tid < EW)
   for (int k = tid; k < r1 - r0; k += EW) {
     const int r = r0 + k;
     float resid;
     if (l == 0) resid = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
-    else resid = P.x[((int64_t)(l - 1) * 2 + 1) * H + r];
-    st_agent(dst + r, resid + res[k]);
+    else resid = P.x[prev + r];
+    st_agent(P.x + dst + r, resid + res[k]);
   }
   vm_signal(P, t);
   return true;
@@ -756,16 +907,19 @@ __device__ __forceinline__ bool task_gateup(const VmParams& P, TaskRef t, float*
   const uint8_t* w = P.wptr[3 + 6 * l + LB_GATEUP];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_MLP_NORM]);
   const float* src = P.x + (int64_t)l * 2 * H;
-  if (!project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, gain))
+  const uint64_t* tsrc = P.tagged ? P.tx + (int64_t)l * 2 * H : nullptr;
+  if (!project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, tsrc, gain))
     return false;
   const float* res = smem + kHead + xs_floats<WFMT>(H);
-  float* dst = P.a + (int64_t)l * F;
+  const int64_t dst = (int64_t)l * F;
   const int tid = opaque_tid();
-  const int EW = epilogue_threads(P);
+  const int EW = P.a_tagged ? kThreads : epilogue_threads(P);
   if (tid < EW)
   for (int k = tid; k < j1 - j0; k += EW) {
     const float g = res[2 * k], u = res[2 * k + 1];
-    st_agent(dst + j0 + k, g / (1.0f + expf(-g)) * u);
+    const float h = g / (1.0f + expf(-g)) * u;
+    if (P.a_tagged) st_tag(P.ta + dst + j0 + k, h, P.tag);
+    else st_agent(P.a + dst + j0 + k, h);
   }
   vm_signal(P, t);
   return true;
@@ -777,16 +931,24 @@ __device__ __forceinline__ bool task_down(const VmParams& P, TaskRef t, float* s
   const int H = P.H, F = P.F;
   const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
   const float* src = P.a + (int64_t)l * F;
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, nullptr)
-                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, F, r0, (r1 - r0) / 2, src, nullptr);
+  const uint64_t* tsrc = P.a_tagged ? P.ta + (int64_t)l * F : nullptr;
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, tsrc, nullptr)
+                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, F, r0, (r1 - r0) / 2, src, tsrc, nullptr);
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(F);
-  const float* mid = P.x + (int64_t)l * 2 * H;
-  float* dst = P.x + ((int64_t)l * 2 + 1) * H;
+  const int64_t mid = (int64_t)l * 2 * H, dst = ((int64_t)l * 2 + 1) * H;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
-  if (tid < EW)
-    for (int k = tid; k < r1 - r0; k += EW) st_agent(dst + r0 + k, mid[r0 + k] + res[k]);
+  if (P.tagged) {  // residual rows (this layer's attention output) are tagged words
+    TagSpin sp;
+    for (int k = tid; k < r1 - r0 && !sp.failed; k += kThreads) {
+      float m[1];
+      if (!ld_tagged<1>(P, P.tx + mid, [](int) { return true; }, [&](int) { return r0 + k; }, m, sp)) break;
+      st_tag(P.tx + dst + r0 + k, m[0] + res[k], P.tag);
+    }
+    if (block_any(sp.failed, smem)) return false;
+  } else if (tid < EW)
+    for (int k = tid; k < r1 - r0; k += EW) st_agent(P.x + dst + r0 + k, P.x[mid + r0 + k] + res[k]);
   vm_signal(P, t);
   return true;
 }
@@ -797,9 +959,11 @@ __device__ __forceinline__ bool task_lmhead(const VmParams& P, TaskRef t, float*
   const int H = P.H;
   const uint8_t* w = P.wptr[2];
   const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
-  const float* src = P.x + ((int64_t)(P.L - 1) * 2 + 1) * H;
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, gain)
-                                : project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, P.V, H, r0, (r1 - r0) / 2, src, gain);
+  const int64_t off = ((int64_t)(P.L - 1) * 2 + 1) * H;
+  const float* src = P.x + off;
+  const uint64_t* tsrc = P.tagged ? P.tx + off : nullptr;
+  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, tsrc, gain)
+                                : project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, P.V, H, r0, (r1 - r0) / 2, src, tsrc, gain);
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(H);
   for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
@@ -858,14 +1022,48 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
   if (!vm_wait(P, t, flag)) return false;
   const bool hv = hh < nh;
   const float scale = 1.0f / sqrtf((float)hd);
+  const bool tagged = P.tagged != 0;
+  const int64_t qoff = (int64_t)l * P.nq * hd + (int64_t)(h0 + (hv ? hh : 0)) * hd + li * 8;
   float q[8];
-  {
-    const float* qp = P.q + (int64_t)l * P.nq * hd + (int64_t)(h0 + (hv ? hh : 0)) * hd + li * 8;
+  // tagged mode: the lane whose positions include pos takes that row's K and
+  // V chunk from the launch's tagged copy (block pblk, chunk pc); no load of
+  // the cache reaches row pos
+  int pblk = -1, pc = 0;
+  u32x4 kp = {0u, 0u, 0u, 0u}, vp = {0u, 0u, 0u, 0u};
+  if (tagged) {
+    const int d = pos - p0 - pw;
+    if (wsc != 0 && pos < p1 && d >= 0 && d % PW == 0 && (d / PW) % kAttnWaves == wsc - 1) {
+      const int bc = d / PW / kAttnWaves;
+      pblk = bc / MAXC;
+      pc = bc % MAXC;
+    }
+    TagSpin sp;
+    float qv[8];
+    if (ld_tagged<8>(P, P.tq + qoff, [](int) { return true; }, [](int k) { return k; }, qv, sp)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = qv[e] * scale;
+      if (pblk >= 0) {
+        const uint64_t* kr = P.tkv + (((int64_t)l * 2 + 0) * P.nkv + g) * hd + li * 8;
+        const uint64_t* vr = P.tkv + (((int64_t)l * 2 + 1) * P.nkv + g) * hd + li * 8;
+        const int64_t vd = vr - kr;
+        float kv[16];
+        if (ld_tagged<16>(P, kr, [](int) { return true; }, [&](int k) { return k < 8 ? (int64_t)k : vd + (k - 8); },
+                          kv, sp)) {
+          auto pack = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u); };
+          kp = u32x4{pack(kv[0], kv[1]), pack(kv[2], kv[3]), pack(kv[4], kv[5]), pack(kv[6], kv[7])};
+          vp = u32x4{pack(kv[8], kv[9]), pack(kv[10], kv[11]), pack(kv[12], kv[13]), pack(kv[14], kv[15])};
+        }
+      }
+    }
+    if (block_any(sp.failed, smem)) return false;
+  } else {
+    const float* qp = P.q + qoff;
     const float4 a = *reinterpret_cast<const float4*>(qp);
     const float4 b = *reinterpret_cast<const float4*>(qp + 4);
     q[0] = a.x * scale; q[1] = a.y * scale; q[2] = a.z * scale; q[3] = a.w * scale;
     q[4] = b.x * scale; q[5] = b.y * scale; q[6] = b.z * scale; q[7] = b.w * scale;
   }
+  if (tagged) trace_mark(P, t, 1);
   float M = -INFINITY, Ls = 0.0f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -920,14 +1118,24 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
     }
     M = nm;
   };
+  auto patch_tag = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (blk == pblk && c == pc) {
+        k[c] = kp;
+        v[c] = vp;
+      }
+  };
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk == 0) patch_pos(ka, va, 0);
+    if (tagged) patch_tag(ka, va, blk);
+    else if (blk == 0) patch_pos(ka, va, 0);
     compute(ka, va, blk);
-    if (blk + 2 < nblk) load_blk(ka, va, blk + 2, false);
+    if (blk + 2 < nblk) load_blk(ka, va, blk + 2, tagged);
     if (blk + 1 < nblk) {
-      if (blk == 0) patch_pos(kb, vb, 1);
+      if (tagged) patch_tag(kb, vb, blk + 1);
+      else if (blk == 0) patch_pos(kb, vb, 1);
       compute(kb, vb, blk + 1);
-      if (blk + 3 < nblk) load_blk(kb, vb, blk + 3, false);
+      if (blk + 3 < nblk) load_blk(kb, vb, blk + 3, tagged);
     }
   }
   // merge the (wave, position group) states of each head through LDS
@@ -964,12 +1172,14 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
     }
   }
   __syncthreads();
-  const int EW = epilogue_threads(P);
+  const int EW = tagged ? kThreads : epilogue_threads(P);
   if (tid < EW) {  // the releasing threads store everything other workgroups read
     for (int i = tid; i < nh * (hd + 2); i += EW) {
       const int hq = i / (hd + 2), e = i - hq * (hd + 2);
       const float v = e < hd ? wout[hq * hd + e] : wout[nh * hd + hq * 2 + (e - hd)];
-      st_agent(P.part + (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2) + e, v);
+      const int64_t o = (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2) + e;
+      if (tagged) st_tag(P.tpart + o, v, P.tag);
+      else st_agent(P.part + o, v);
     }
   }
   return true;
@@ -997,12 +1207,13 @@ __device__ __forceinline__ bool task_attn(const VmParams& P, TaskRef t, float* s
     int* flag = reinterpret_cast<int*>(smem + kWaves);
     if (!vm_wait(P, t, flag)) return false;
     const int tid = opaque_tid();
-    const int EW = epilogue_threads(P);
+    const int EW = P.tagged ? kThreads : epilogue_threads(P);
     if (tid < EW)
       for (int i = tid; i < grp * (hd + 2); i += EW) {
         const int hh = i / (hd + 2), e = i - hh * (hd + 2);
-        float* dst = P.part + (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2);
-        st_agent(dst + e, e == hd ? -INFINITY : 0.0f);
+        const int64_t o = (((int64_t)l * P.nq + g * grp + hh) * S + s) * (hd + 2) + e;
+        if (P.tagged) st_tag(P.tpart + o, e == hd ? -INFINITY : 0.0f, P.tag);
+        else st_agent(P.part + o, e == hd ? -INFINITY : 0.0f);
       }
   } else {
     // GP = heads per pass: the group size rounded up to a power of two,
@@ -1038,19 +1249,43 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
   float* red = smem;
   const int hd = P.hd, hq = hd >> 2, tid = opaque_tid();
   if (!vm_wait(P, t, flag)) return false;
-  const float* part = P.part + ((int64_t)l * P.nq + h) * S * (hd + 2);
+  const int64_t pbase = ((int64_t)l * P.nq + h) * S * (hd + 2);
+  const float* part = P.part + pbase;
   float* wsum = smem + P.lds_att;  // [S][hd] scaled chunks
   float* wts = wsum + S * hd;      // [S]
   float2 ml = make_float2(-INFINITY, 0.0f);
-  if (tid < S) ml = *reinterpret_cast<const float2*>(part + (int64_t)tid * (hd + 2) + hd);
   const int items = S * hq;
   float4 ch[4];
+  if (P.tagged) {
+    // the partials are tagged words: one round of reads (this thread's four
+    // chunks and its split's (max, sum)), then re-reads until tagged.  The
+    // engine admits the tagged mode only where S <= kThreads and
+    // S * hd / 4 <= 4 * kThreads, so these cover every item.
+    const uint64_t* tp = P.tpart + pbase;
+    TagSpin spn;
+    float v[18];
+    ld_tagged<18>(
+        P, tp, [&](int k) { return k < 16 ? tid + (k >> 2) * kThreads < items : tid < S; },
+        [&](int k) {
+          if (k >= 16) return (int64_t)tid * (hd + 2) + hd + (k - 16);
+          const int it = tid + (k >> 2) * kThreads, sp = it / hq, qd = it - sp * hq;
+          return (int64_t)sp * (hd + 2) + qd * 4 + (k & 3);
+        },
+        v, spn);
+    if (block_any(spn.failed, red)) return false;
+    trace_mark(P, t, 1);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int it = tid + k * kThreads;
-    if (it < items) {
-      const int sp = it / hq, qd = it - sp * hq;
-      ch[k] = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
+    for (int k = 0; k < 4; ++k) ch[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    if (tid < S) ml = make_float2(v[16], v[17]);
+  } else {
+    if (tid < S) ml = *reinterpret_cast<const float2*>(part + (int64_t)tid * (hd + 2) + hd);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int it = tid + k * kThreads;
+      if (it < items) {
+        const int sp = it / hq, qd = it - sp * hq;
+        ch[k] = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
+      }
     }
   }
   float m = ml.x;
@@ -1098,7 +1333,9 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
     for (int e = tid; e < hd; e += EW) {
       float v = 0.0f;
       for (int sp = 0; sp < S; ++sp) v += wsum[sp * hd + e];
-      st_agent(P.o + (int64_t)l * P.nq * hd + (int64_t)h * hd + e, v * inv);
+      const int64_t o = (int64_t)l * P.nq * hd + (int64_t)h * hd + e;
+      if (P.tagged) st_tag(P.to + o, v * inv, P.tag);
+      else st_agent(P.o + o, v * inv);
     }
   vm_signal(P, t);
   return true;
@@ -1300,6 +1537,10 @@ struct amk_engine {
   int wallclock_khz = 100000;
   int32_t n_tasks = 0;
   uint64_t* d_trace = nullptr;  // allocated on first amk_engine_set_trace(e, 1)
+  // tagged activations: one arena, zeroed at creation (tag 0 is never a launch's)
+  uint64_t* tag_arena = nullptr;
+  size_t tag_arena_words = 0;
+  std::vector<size_t> tag_words;
 };
 
 namespace amk {
@@ -1591,6 +1832,28 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
       (st = dev_alloc(e, &pr.ctr, (size_t)std::max(1, s->n_counters) * kCounterStride)) != AMK_OK ||
       (st = dev_alloc(e, &pr.err, 64)) != AMK_OK)
     return bail(st);
+  pr.tagged = c.sync_mode != 0;
+  pr.a_tagged = c.sync_mode == 1;
+  pr.tag = 1;
+  if (pr.tagged) {
+    const int64_t nkvd = (int64_t)m.n_kv_heads * hd;
+    size_t n = 0;
+    e->tag_words.clear();
+    for (int64_t w : {L * 2 * H, L * qd, L * 2 * nkvd, L * m.n_heads * S * (hd + 2), L * qd, L * F}) {
+      e->tag_words.push_back((size_t)w);
+      n += (size_t)w;
+    }
+    uint64_t* arena = nullptr;
+    if ((st = dev_alloc(e, &arena, n)) != AMK_OK) return bail(st);
+    e->tag_arena = arena;
+    e->tag_arena_words = n;
+    uint64_t** dst[] = {&pr.tx, &pr.tq, &pr.tkv, &pr.tpart, &pr.to, &pr.ta};
+    size_t off = 0;
+    for (int k = 0; k < 6; ++k) {
+      *dst[k] = arena + off;
+      off += e->tag_words[k];
+    }
+  }
   pr.tasks = d_tasks;
   pr.queue_off = d_qoff;
   pr.queue = d_queue;
@@ -1631,12 +1894,19 @@ amk_status amk_decode_step(amk_engine* e, int32_t token, int32_t pos, void* stre
     HIP_TRY(hipMemsetAsync(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
     e->params.epoch = 0;
   }
+  // a launch's tag is never reused while words of an earlier launch may hold
+  // it: at the wrap the arena is cleared and tags start again from 1
+  if (e->params.tagged && e->params.tag == 0xFFFFFFFFu) {
+    HIP_TRY(hipMemsetAsync(e->tag_arena, 0, e->tag_arena_words * sizeof(uint64_t), st));
+    e->params.tag = 1;
+  }
   e->params.token = token;
   e->params.pos = pos;
   void* args[] = {&e->params};
   HIP_TRY(hipLaunchCooperativeKernel(e->kernel, dim3(e->config.num_cus), dim3(kThreads), args,
                                      (unsigned)e->lds_bytes, st));
   e->params.epoch += 1;
+  e->params.tag += 1;
   e->written = (int64_t)pos + 1;
   e->steps += 1;
   return AMK_OK;

@@ -29,6 +29,9 @@ SPACE = [
     ("poll_mode", [0, 1]),
     ("cu_policy", [0, 1]),
     ("release_mode", [0, 1]),
+    ("sync_mode", [0, 1, 2]),
+    ("merge_place", [0, 1]),
+    ("prefetch_attn_kb", [-1, 64, 128]),
 ]
 
 REL_L2 = 1e-2

@@ -151,6 +151,7 @@ def test_default_config_resolves_every_field():
     assert d["num_cus"] == 256 and d["wg_threads"] == 512 and d["pipeline_depth"] in (4, 8, 16)
     assert all(d[k] == 256 for k in ("tiles_qkv", "tiles_o", "tiles_gateup", "tiles_down", "tiles_lm"))
     assert d["attn_splits"] == 3 * 256 // (4 * 8) and d["prefetch_kb"] == 64
+    assert d["sync_mode"] == 1 and d["merge_place"] == 0 and d["prefetch_attn_kb"] == 1024
 
 
 def test_packed_ids_out_of_range():
@@ -223,3 +224,21 @@ def test_merge_tasks_avoid_attention_queues():
     c = amk.default_schedule_config(m, 256)
     c.prefetch_attn_kb = -2
     expect_status(amk.ERR_INVALID_ARG, amk.Schedule.build, m, c)
+
+
+def test_sync_mode_limits():
+    m = amk.ModelConfig.from_workload(synth.get("8b"))
+    for mode, splits, code in ((3, 24, amk.ERR_UNSUPPORTED), (1, 65, amk.ERR_UNSUPPORTED),
+                               (2, 65, amk.ERR_UNSUPPORTED), (-1, 24, amk.ERR_UNSUPPORTED)):
+        c = amk.default_schedule_config(m, 256)
+        c.sync_mode, c.attn_splits = mode, splits
+        expect_status(code, amk.Schedule.build, m, c)
+    for mode in (0, 1, 2):
+        c = amk.default_schedule_config(m, 256)
+        c.sync_mode, c.attn_splits = mode, 64
+        s = amk.Schedule.build(m, c)
+        assert s.validate() == (0, -1, -1, -1)
+        s.close()
+    # the default falls back to counters where the split count is too large
+    c = amk.default_schedule_config(amk.ModelConfig.from_workload(synth.get("8b").with_(n_kv_heads=1, n_heads=16)), 256)
+    assert c.sync_mode == 0

@@ -68,10 +68,13 @@ def test_engine_refuses_unsafe_and_foreign_schedules(tiny):
     expect_status(amk.ERR_UNSUPPORTED, amk.Engine, sch, dev_w, kv, logits)
 
 
-def test_timeout_is_reported_and_the_engine_recovers(tiny):
+@pytest.mark.parametrize("sync_mode", [0, 1])
+def test_timeout_is_reported_and_the_engine_recovers(tiny, sync_mode):
+    """Both wait protocols (counters, tagged words) give up at the spin
+    budget, report it, and decode correctly afterwards."""
     wl, w = tiny
     toks = synth.tokens(2, 12, wl.vocab)
-    eng = make_engine(wl, w)
+    eng = make_engine(wl, w, {"sync_mode": sync_mode})
     orc = oracle.Model(wl, w)
     kv_o = orc.new_kv()
     for p in range(8):

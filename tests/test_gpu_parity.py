@@ -98,8 +98,12 @@ def test_full_size_long_context(name, w8b):
 
 
 @pytest.mark.parametrize("sched", [{"prefetch_kb": -1}, {"prefetch_kb": 4}, {"poll_mode": 1},
+                                   {"sync_mode": 0}, {"sync_mode": 0, "poll_mode": 1},
+                                   {"sync_mode": 0, "release_mode": 1}, {"sync_mode": 0, "attn_splits": 3},
                                    {"release_mode": 1}, {"pipeline_depth": 4}, {"pipeline_depth": 16},
-                                   {"cu_policy": 1}, {"attn_splits": 3}],
+                                   {"cu_policy": 1}, {"attn_splits": 3}, {"merge_place": 1},
+                                   {"sync_mode": 1}, {"sync_mode": 2}, {"sync_mode": 1, "attn_splits": 3},
+                                   {"sync_mode": 1, "prefetch_kb": -1, "prefetch_attn_kb": -1}],
                          ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_schedule_knobs_keep_parity(sched):
     """Every ScheduleConfig knob the kernel reads, on the tiny decoder's full
@@ -123,3 +127,42 @@ def test_tuner_keeps_only_safe_agreeing_faster_configs():
         if h.get("kept"):
             assert h["parity"] and "error" not in h
     log(f"tuner tiny: best {res['best']} {res['ms']:.4f} ms vs {res['reference_ms']:.4f} ms")
+
+
+@pytest.mark.parametrize("name", ["8b", "8b_int4"])
+def test_tagged_sync_is_bit_identical(name, w8b):
+    """sync_mode 1 and 2 (tagged activations) run the same arithmetic as the
+    counter protocol: logits bit-identical over a few steps after a seeded
+    KV prefix, at full size."""
+    import torch
+
+    import persistent_megakernel_wg_amd as amk
+    from tests.gpu_common import device_cus
+    wl = synth.get(name)
+    m = amk.ModelConfig.from_workload(wl)
+    dev_w = amk.upload_model(m, w8b)
+    P = 100
+    kvp = torch.from_numpy(synth.kv_prefix(wl, P, seed=3).view(np.int16).reshape(-1)).cuda()
+    toks = synth.tokens(2, P + 4, wl.vocab)[P:]
+    outs = []
+    for mode in (0, 1, 2):
+        cfg = amk.default_schedule_config(m, device_cus())
+        cfg.sync_mode = mode
+        sched = amk.Schedule.build(m, cfg)
+        kv, logits = amk.alloc_state(m)
+        kv.copy_(kvp)
+        eng = amk.Engine(sched, dev_w, kv, logits)
+        eng.set_kv_length(P)
+        got = []
+        for i, tok in enumerate(toks):
+            eng.decode_step(int(tok), P + i)
+            torch.cuda.synchronize()
+            eng.check()
+            got.append(logits.cpu().numpy().copy())
+        outs.append(np.stack(got))
+        eng.close()
+        sched.close()
+        del kv, logits
+    for k in (1, 2):
+        assert np.array_equal(outs[0].view(np.uint32), outs[k].view(np.uint32)), k
+    log(f"{name}: sync_mode 1 and 2 bit-identical to sync_mode 0 over {len(toks)} steps")
