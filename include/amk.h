@@ -83,7 +83,9 @@ typedef struct {
   /* Queue-walk knobs (no effect on the DAG the safety gate checks):
    * poll_mode 0: the polling wave issues its weight prologue before the
    *   wait like the others; 1: after the wait (its poll is then not queued
-   *   behind its own loads).
+   *   behind its own loads); 2: every wave issues half of its ring before
+   *   the wait and half once the wait is over, so that loads issued after
+   *   the input arrived keep HBM busy while the input is staged.
    * prefetch_kb: LDS kilobytes per task into which the end of the previous
    *   task of the queue copies the task's first weight slabs (LDS DMA), so
    *   streaming goes on through waits; 0 = 64 KB (the measured best on
@@ -93,11 +95,12 @@ typedef struct {
    *   release; 1: the epilogue stores and the release are issued by the
    *   polling wave alone while the others start the next task. */
   int32_t poll_mode, release_mode, prefetch_kb;
-  /* Relative work per XCD (permille; 0 = 1000): the GEMV rows of every phase
-   * are split over the queues in proportion to the weight of the XCD that
-   * runs each queue (queue c runs on XCD c % 8, the round-robin placement of
-   * workgroups over the 8 XCDs), to even out XCD speed differences. */
-  int32_t xcd_weight[8];
+  /* Relative work per XCD and GEMV phase (permille; 0 = 1000), indexed
+   * [AMK_PHASE_*][xcd]: the rows of each phase are split over the queues in
+   * proportion to the weight of the XCD that runs each queue (queue c runs
+   * on XCD c % 8, the round-robin placement of workgroups over the 8 XCDs),
+   * to even out XCD speed differences, which differ from phase to phase. */
+  int32_t xcd_weight[5][8];
   /* Share (permille; 0 = default 1000) of an even O-projection tile given to
    * queues that also run a MERGE task of the layer: those queues reach the
    * O-projection late, so they get fewer of its rows. */
@@ -128,6 +131,8 @@ typedef struct {
    * 1 and 2 need attn_splits <= 512 and attn_splits * head_dim <= 8192. */
   int32_t sync_mode;
 } amk_schedule_config;
+
+enum { AMK_PHASE_QKV = 0, AMK_PHASE_O = 1, AMK_PHASE_GATEUP = 2, AMK_PHASE_DOWN = 3, AMK_PHASE_LM = 4 };
 
 #define AMK_FUSE_NORM_PROLOGUE 0x1u  /* RMSNorm recomputed inside each GEMV task */
 #define AMK_FUSE_ROPE_KV 0x2u        /* RoPE + KV append in the QKV task */

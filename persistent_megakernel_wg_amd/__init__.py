@@ -58,11 +58,12 @@ class ScheduleConfig(ctypes.Structure):
     _fields_ = [(n, _i32) for n in ("num_cus", "wg_threads", "tiles_qkv", "tiles_o",
                                     "tiles_gateup", "tiles_down", "tiles_lm", "attn_splits",
                                     "cu_policy", "pipeline_depth")] + [("fuse_flags", _u32)] + [
-        (n, _i32) for n in ("poll_mode", "release_mode", "prefetch_kb")] + [("xcd_weight", _i32 * 8), ("merge_o_share", _i32),
+        (n, _i32) for n in ("poll_mode", "release_mode", "prefetch_kb")] + [("xcd_weight", (_i32 * 8) * 5), ("merge_o_share", _i32),
         ("merge_place", _i32), ("prefetch_attn_kb", _i32), ("sync_mode", _i32)]
 
     def as_dict(self):
-        return {n: (list(getattr(self, n)) if n == "xcd_weight" else getattr(self, n)) for n, _ in self._fields_}
+        return {n: ([list(r) for r in getattr(self, n)] if n == "xcd_weight" else getattr(self, n))
+                for n, _ in self._fields_}
 
 
 class TaskDesc(ctypes.Structure):

@@ -64,14 +64,16 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.pipeline_depth == 0) c.pipeline_depth = 8;
   if (c.pipeline_depth != 4 && c.pipeline_depth != 8 && c.pipeline_depth != 16)
     return fail(AMK_ERR_UNSUPPORTED, "pipeline_depth must be 4, 8 or 16");
-  if (c.poll_mode != 0 && c.poll_mode != 1) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0 or 1");
+  if (c.poll_mode < 0 || c.poll_mode > 2) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0, 1 or 2");
   if (c.release_mode != 0 && c.release_mode != 1)
     return fail(AMK_ERR_UNSUPPORTED, "release_mode must be 0 or 1");
-  for (int32_t x = 0; x < 8; ++x) {
-    if (c.xcd_weight[x] == 0) c.xcd_weight[x] = 1000;
-    if (c.xcd_weight[x] < 100 || c.xcd_weight[x] > 10000)
-      return fail(AMK_ERR_INVALID_ARG, "xcd_weight must be 0 (default) or 100..10000 permille");
-  }
+  for (int32_t ph = 0; ph < 5; ++ph)
+    for (int32_t x = 0; x < 8; ++x) {
+      int32_t& w = c.xcd_weight[ph][x];
+      if (w == 0) w = 1000;
+      if (w < 100 || w > 10000)
+        return fail(AMK_ERR_INVALID_ARG, "xcd_weight must be 0 (default) or 100..10000 permille");
+    }
   if (c.merge_o_share == 0) c.merge_o_share = 1000;
   if (c.merge_o_share < 1 || c.merge_o_share > 1000)
     return fail(AMK_ERR_INVALID_ARG, "merge_o_share must be 0 (default) or 1..1000 permille");

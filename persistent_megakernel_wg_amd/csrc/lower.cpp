@@ -39,11 +39,12 @@ struct Builder {
 
   // bounds of T tiles over n items (in groups of `grain`), each tile's share
   // proportional to the weight of the XCD its queue runs on
-  std::vector<int64_t> bounds(int64_t n, int64_t T, int64_t grain, const std::vector<char>* light = nullptr) const {
+  std::vector<int64_t> bounds(int phase, int64_t n, int64_t T, int64_t grain,
+                              const std::vector<char>* light = nullptr) const {
     std::vector<int64_t> w(T), b(T + 1);
     int64_t tot = 0;
     for (int64_t i = 0; i < T; ++i) {
-      w[i] = c.xcd_weight[cu_of(i, T) % 8];
+      w[i] = c.xcd_weight[phase][cu_of(i, T) % 8];
       if (light && (*light)[cu_of(i, T)]) w[i] = w[i] * c.merge_o_share / 1000;
       tot += w[i];
     }
@@ -110,8 +111,10 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
     };
     std::vector<char> merges(c.num_cus, 0);
     for (int32_t h = 0; h < nq; ++h) merges[merge_cu(h)] = 1;
-    const std::vector<int64_t> bq = b.bounds(U, c.tiles_qkv, 1), bo = b.bounds(m.hidden, c.tiles_o, 2, &merges),
-                               bg = b.bounds(m.ffn, c.tiles_gateup, 1), bd = b.bounds(m.hidden, c.tiles_down, 2);
+    const std::vector<int64_t> bq = b.bounds(AMK_PHASE_QKV, U, c.tiles_qkv, 1),
+                               bo = b.bounds(AMK_PHASE_O, m.hidden, c.tiles_o, 2, &merges),
+                               bg = b.bounds(AMK_PHASE_GATEUP, m.ffn, c.tiles_gateup, 1),
+                               bd = b.bounds(AMK_PHASE_DOWN, m.hidden, c.tiles_down, 2);
     for (int32_t i = 0; i < c.tiles_qkv; ++i) {
       const int32_t u0 = (int32_t)bq[i], u1 = (int32_t)bq[i + 1];
       if (l == 0) b.add(AMK_TASK_QKV, b.cu_of(i, c.tiles_qkv), {l, u0, u1}, {}, {c_qkv});
@@ -138,7 +141,7 @@ amk_status lower(const amk_model_config& m, const amk_schedule_config& c, amk_sc
     prev_down = c_down;
   }
   const int32_t c_lm = b.counter();
-  const std::vector<int64_t> bl = b.bounds(m.vocab, c.tiles_lm, 2);
+  const std::vector<int64_t> bl = b.bounds(AMK_PHASE_LM, m.vocab, c.tiles_lm, 2);
   for (int32_t i = 0; i < c.tiles_lm; ++i)
     b.add(AMK_TASK_LMHEAD, b.cu_of(i, c.tiles_lm), {(int32_t)bl[i], (int32_t)bl[i + 1]},
           {{prev_down, Pd}}, {c_lm});

@@ -643,7 +643,7 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uin
 template <class F, int DS, int RPU, typename StageFn>
 __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
                                      uint32_t meta_row_bytes, int nunits, int K, const float* xs,
-                                     const float* csum, float* tbl, bool poll_late, int pf_steps,
+                                     const float* csum, float* tbl, int poll_late, int pf_steps,
                                      const uint8_t* pf, StageFn&& stage) {
   const int tid = opaque_tid(), lane = tid & 63;
   const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -671,17 +671,21 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
     }
     it.advance();
   };
-  auto prologue = [&] {
+  // ring slots [0, split) are loaded before the wait, the rest after it
+  // (poll_late 1: none for the polling wave; 2: half of the ring for every
+  // wave, so loads issued after the input has arrived keep streaming while
+  // the input is staged)
+  const int split = poll_late == 2 ? DS / 2 : (poll_late == 1 && sw == 0 ? 0 : DS);
+  auto prologue = [&](bool first) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      issue(buf[s], mbuf[s]);
+      if ((s < split) == first) issue(buf[s], mbuf[s]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const bool late = poll_late && sw == 0;
-  if (!late) prologue();
+  prologue(true);
   stage();
-  if (late) prologue();
+  prologue(false);
   if (n > 0) {
     StepIter c;
     c.init(sw, nunits, J);
@@ -782,12 +786,18 @@ __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* sme
   // waves) before its ring prologue: waiting until only the prologue's loads
   // may be outstanding means those DMAs are done; the barrier after it shows
   // the data to every wave.
+  // (poll_mode 2 issues only half of the ring before the wait.)
   constexpr int kPrologueLoads = DS * RPU * (F::kMeta ? 2 : 1);
+  constexpr int kHalfPrologueLoads = (DS / 2) * RPU * (F::kMeta ? 2 : 1);
   const bool pf_wait = t.pf_have > 0 && opaque_tid() >= 64;
-  gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late != 0,
+  const bool half = P.poll_late == 2;
+  gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late,
                    t.pf_have, reinterpret_cast<const uint8_t*>(smem) + t.pf_lds, [&] {
     ok = vm_wait(P, t, flag, [&] {
-      if (pf_wait) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
+      if (pf_wait) {
+        if (half) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kHalfPrologueLoads) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
+      }
     });
     if (ok) ok = stage_x<F, SRC_BF16, NORM>(P, src, tsrc, K, gain, xs, red, xsum, csum);
     if (ok && P.tagged) trace_mark(P, t, 1);

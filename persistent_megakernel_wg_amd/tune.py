@@ -12,6 +12,10 @@ knobs of ScheduleConfig in a fixed order; every candidate must
   3. be faster than the best so far by more than `min_gain` (median
      kernel time over `steps` timed decode steps).
 
+After the knobs, the per-phase XCD weights are fitted from traced steps
+(tasks of an XCD that ends late get proportionally fewer rows) and kept
+under the same three conditions.
+
 Usage (one GPU):  python -m persistent_megakernel_wg_amd.tune --workload 8b --out best.json
 """
 import argparse
@@ -47,7 +51,11 @@ def apply(cfg, overrides):
         if isinstance(v, list):
             arr = getattr(cfg, k)
             for i, x in enumerate(v):
-                arr[i] = x
+                if isinstance(x, list):
+                    for j, y in enumerate(x):
+                        arr[i][j] = y
+                else:
+                    arr[i] = x
         else:
             setattr(cfg, k, v)
     return cfg
@@ -113,6 +121,51 @@ class Bench:
             sched.close()
         return ms, out
 
+    def xcd_imbalance(self, overrides, nsteps=4):
+        """Per GEMV phase and XCD, from traced decode steps: the mean offset
+        of a task's end from the median end of its phase, and its mean
+        duration from input staged to end (microseconds).  [5][8] each."""
+        torch, amk = self.torch, self.amk
+        sched = amk.Schedule.build(self.model, self.config(overrides))
+        eng = amk.Engine(sched, self.dev_w, self.kv, self.logits)
+        s = torch.cuda.current_stream()
+        tasks = sched.view()["tasks"]
+        ty = np.array([t["type"] for t in tasks])
+        cu = np.array([t["cu"] for t in tasks])
+        layer = np.array([t["p"][0] if t["type"] != 7 else -1 for t in tasks])
+        off = np.zeros((5, 8))
+        dur = np.zeros((5, 8))
+        cnt = np.zeros((5, 8))
+        try:
+            self.kv.copy_(self.kvp)
+            eng.set_kv_length(self.P)
+            for i in range(2):
+                eng.decode_step(int(self.toks[i]), self.P + i, s)
+            eng.set_trace(True)
+            for i in range(nsteps):
+                eng.decode_step(int(self.toks[i]), self.P + i, s)
+                torch.cuda.synchronize()
+                eng.check()
+                st, khz = eng.read_trace(len(tasks))
+                st = st.astype(np.float64) * (1e3 / khz)
+                for ph, tt in enumerate((1, 4, 5, 6, 7)):
+                    layers = [-1] if tt == 7 else range(1, self.model.n_layers - 1)
+                    for l in layers:
+                        m = (ty == tt) & (layer == l)
+                        if not m.any():
+                            continue
+                        end = st[m, 3]
+                        x = cu[m] % 8
+                        np.add.at(off[ph], x, end - np.median(end))
+                        np.add.at(dur[ph], x, st[m, 3] - st[m, 1])
+                        np.add.at(cnt[ph], x, 1)
+        finally:
+            eng.set_trace(False)
+            eng.close()
+            sched.close()
+        cnt = np.maximum(cnt, 1)
+        return off / cnt, dur / cnt
+
     def agrees(self, out):
         for g, o in zip(out, self.reference):
             rel = np.linalg.norm(g - o) / np.linalg.norm(o)
@@ -122,7 +175,7 @@ class Bench:
         return True, 0.0
 
 
-def tune(wl, min_gain=0.005, steps=48, space=SPACE):
+def tune(wl, min_gain=0.005, steps=48, space=SPACE, xcd_rounds=2):
     b = Bench(wl, steps=steps)
     default = b.config({})
     best = {}
@@ -148,6 +201,28 @@ def tune(wl, min_gain=0.005, steps=48, space=SPACE):
             log(f"{cand}: {ms:.4f} ms parity {'ok' if ok else 'FAIL %.2e' % rel}{' KEEP' if kept else ''}")
             if kept:
                 best, best_ms = cand, ms
+    # per-phase XCD weights: shorten the tasks of XCDs that end late and
+    # lengthen those that end early, in proportion to their durations
+    for rnd in range(xcd_rounds):
+        off, dur = b.xcd_imbalance(best)
+        cur = np.array([list(r) for r in b.config(best).xcd_weight], dtype=np.float64)
+        new = cur * np.clip((dur - (off - off.mean(axis=1, keepdims=True))) / np.maximum(dur, 1e-3), 0.7, 1.3)
+        new = np.clip(np.round(new / new.mean(axis=1, keepdims=True) * 1000), 100, 10000).astype(int)
+        cand = dict(best)
+        cand["xcd_weight"] = new.tolist()
+        log(f"xcd end offsets (us) per phase: {np.round(off, 2).tolist()}")
+        try:
+            ms, out = b.run(cand)
+        except Exception as e:
+            history.append({"overrides": cand, "error": str(e), "kept": False})
+            break
+        ok, rel = b.agrees(out)
+        kept = ok and ms < best_ms * (1 - min_gain)
+        history.append({"overrides": cand, "ms": ms, "parity": ok, "kept": kept})
+        log(f"xcd weights round {rnd}: {ms:.4f} ms parity {'ok' if ok else 'FAIL'}{' KEEP' if kept else ''}")
+        if not kept:
+            break
+        best, best_ms = cand, ms
     # re-measure the winner against the reference, interleaved
     ref, win = [], []
     for _ in range(2):

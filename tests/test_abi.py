@@ -138,7 +138,7 @@ def test_invalid_schedule_configs():
     for field, value, code in [("pipeline_depth", 5, amk.ERR_UNSUPPORTED), ("attn_splits", 300, amk.ERR_UNSUPPORTED),
                                ("cu_policy", 2, amk.ERR_UNSUPPORTED), ("fuse_flags", 0x3, amk.ERR_UNSUPPORTED),
                                ("wg_threads", 256, amk.ERR_UNSUPPORTED), ("num_cus", 0, amk.ERR_INVALID_ARG),
-                               ("poll_mode", 2, amk.ERR_UNSUPPORTED), ("release_mode", 3, amk.ERR_UNSUPPORTED)]:
+                               ("poll_mode", 3, amk.ERR_UNSUPPORTED), ("release_mode", 3, amk.ERR_UNSUPPORTED)]:
         c = amk.default_schedule_config(m, 8)
         setattr(c, field, value)
         expect_status(code, amk.Schedule.build, m, c)
@@ -187,7 +187,8 @@ def test_xcd_weights_shift_rows_and_stay_safe():
     c = amk.default_schedule_config(m, 256)
     base = amk.Schedule.build(m, c).view()
     for x in range(8):
-        c.xcd_weight[x] = 900 if x % 2 else 1100
+        c.xcd_weight[2][x] = 900 if x % 2 else 1100   # gate/up
+        c.xcd_weight[4][x] = 900 if x % 2 else 1100   # LM head
     sch = amk.Schedule.build(m, c)
     assert sch.validate() == (0, -1, -1, -1)
     v = sch.view()
@@ -199,8 +200,11 @@ def test_xcd_weights_shift_rows_and_stay_safe():
         even = np.mean([r for cu, r in rows.items() if cu % 2 == 0])
         odd = np.mean([r for cu, r in rows.items() if cu % 2 == 1])
         assert abs(even / odd - 1100 / 900) < 0.03, (ty, even, odd)
+    # the other phases keep the even split
+    qkv = {t["cu"]: t["p"][2] - t["p"][1] for t in v["tasks"] if t["type"] == 1 and t["p"][0] == 0}
+    assert max(qkv.values()) - min(qkv.values()) <= 1
     assert len(base["tasks"]) == len(v["tasks"])
-    c.xcd_weight[3] = 50
+    c.xcd_weight[3][3] = 50
     expect_status(amk.ERR_INVALID_ARG, amk.Schedule.build, m, c)
 
 

@@ -20,5 +20,6 @@ def test_space_knobs_exist_and_candidates_are_safe():
 
 def test_apply_sets_array_knobs_elementwise():
     m = amk.ModelConfig.from_workload(synth.get("8b"))
-    c = tune.apply(amk.default_schedule_config(m, 256), {"xcd_weight": [900, 1100] * 4, "attn_splits": 24})
-    assert list(c.xcd_weight) == [900, 1100] * 4 and c.attn_splits == 24
+    w = [[1000] * 8, [1000] * 8, [900, 1100] * 4, [1000] * 8, [1000] * 8]
+    c = tune.apply(amk.default_schedule_config(m, 256), {"xcd_weight": w, "attn_splits": 24})
+    assert [list(r) for r in c.xcd_weight] == w and c.attn_splits == 24
