@@ -880,12 +880,17 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* 
   const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
   const float* src = P.o + (int64_t)l * qd;
   const uint64_t* tsrc = P.tagged ? P.to + (int64_t)l * qd : nullptr;
+  const int64_t dst = (int64_t)l * 2 * H, prev = ((int64_t)(l - 1) * 2 + 1) * H;
+  // tagged: the first residual row of each thread, read before the weight
+  // stream so that it is not queued behind it (the previous layer's output,
+  // complete once this queue's own QKV task staged it; checked anyway)
+  uint64_t rres = 0;
+  if (P.tagged && l > 0 && opaque_tid() < r1 - r0) rres = ld_tag(P.tx + prev + r0 + opaque_tid());
   // rows go in pairs when the count is even (two loads per step), else singly
   const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, tsrc, nullptr)
                                 : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, qd, r0, (r1 - r0) / 2, src, tsrc, nullptr);
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(qd);
-  const int64_t dst = (int64_t)l * 2 * H, prev = ((int64_t)(l - 1) * 2 + 1) * H;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
   if (P.tagged) {  // residual rows of the previous layer's output are tagged words too
@@ -894,6 +899,7 @@ __device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* 
       const int r = r0 + k;
       float resid[1];
       if (l == 0) resid[0] = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
+      else if (k == tid && (uint32_t)(rres >> 32) == P.tag) resid[0] = tag_val(rres);
       else if (!ld_tagged<1>(P, P.tx + prev, [](int) { return true; }, [&](int) { return r; }, resid, sp)) break;
       st_tag(P.tx + dst + r, resid[0] + res[k], P.tag);
     }
@@ -942,18 +948,24 @@ __device__ __forceinline__ bool task_down(const VmParams& P, TaskRef t, float* s
   const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
   const float* src = P.a + (int64_t)l * F;
   const uint64_t* tsrc = P.a_tagged ? P.ta + (int64_t)l * F : nullptr;
+  const int64_t mid = (int64_t)l * 2 * H, dst = ((int64_t)l * 2 + 1) * H;
+  // tagged: the first residual row of each thread, read ahead of the weight
+  // stream (this layer's attention output, complete once this queue's own
+  // gate/up task staged it; checked anyway)
+  uint64_t rres = 0;
+  if (P.tagged && opaque_tid() < r1 - r0) rres = ld_tag(P.tx + mid + r0 + opaque_tid());
   const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, tsrc, nullptr)
                                 : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, F, r0, (r1 - r0) / 2, src, tsrc, nullptr);
   if (!ok) return false;
   const float* res = smem + kHead + xs_floats<WFMT>(F);
-  const int64_t mid = (int64_t)l * 2 * H, dst = ((int64_t)l * 2 + 1) * H;
   const int tid = opaque_tid();
   const int EW = epilogue_threads(P);
   if (P.tagged) {  // residual rows (this layer's attention output) are tagged words
     TagSpin sp;
     for (int k = tid; k < r1 - r0 && !sp.failed; k += kThreads) {
       float m[1];
-      if (!ld_tagged<1>(P, P.tx + mid, [](int) { return true; }, [&](int) { return r0 + k; }, m, sp)) break;
+      if (k == tid && (uint32_t)(rres >> 32) == P.tag) m[0] = tag_val(rres);
+      else if (!ld_tagged<1>(P, P.tx + mid, [](int) { return true; }, [&](int) { return r0 + k; }, m, sp)) break;
       st_tag(P.tx + dst + r0 + k, m[0] + res[k], P.tag);
     }
     if (block_any(sp.failed, smem)) return false;
@@ -1047,23 +1059,19 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
       pblk = bc / MAXC;
       pc = bc % MAXC;
     }
+    // q and, for the lane holding pos, that row's K and V chunks: one round
+    // of reads (both live in the tagged arena, addressed from q's base)
     TagSpin sp;
-    float qv[8];
-    if (ld_tagged<8>(P, P.tq + qoff, [](int) { return true; }, [](int k) { return k; }, qv, sp)) {
+    const int64_t kd = (P.tkv - P.tq) + (((int64_t)l * 2 + 0) * P.nkv + g) * hd + li * 8 - qoff;
+    const int64_t vd = (P.tkv - P.tq) + (((int64_t)l * 2 + 1) * P.nkv + g) * hd + li * 8 - qoff;
+    float v[24];
+    if (ld_tagged<24>(P, P.tq + qoff, [&](int k) { return k < 8 || pblk >= 0; },
+                      [&](int k) { return k < 8 ? (int64_t)k : (k < 16 ? kd + (k - 8) : vd + (k - 16)); }, v, sp)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = qv[e] * scale;
-      if (pblk >= 0) {
-        const uint64_t* kr = P.tkv + (((int64_t)l * 2 + 0) * P.nkv + g) * hd + li * 8;
-        const uint64_t* vr = P.tkv + (((int64_t)l * 2 + 1) * P.nkv + g) * hd + li * 8;
-        const int64_t vd = vr - kr;
-        float kv[16];
-        if (ld_tagged<16>(P, kr, [](int) { return true; }, [&](int k) { return k < 8 ? (int64_t)k : vd + (k - 8); },
-                          kv, sp)) {
-          auto pack = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u); };
-          kp = u32x4{pack(kv[0], kv[1]), pack(kv[2], kv[3]), pack(kv[4], kv[5]), pack(kv[6], kv[7])};
-          vp = u32x4{pack(kv[8], kv[9]), pack(kv[10], kv[11]), pack(kv[12], kv[13]), pack(kv[14], kv[15])};
-        }
-      }
+      for (int e = 0; e < 8; ++e) q[e] = v[e] * scale;
+      auto pack = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u); };
+      kp = u32x4{pack(v[8], v[9]), pack(v[10], v[11]), pack(v[12], v[13]), pack(v[14], v[15])};
+      vp = u32x4{pack(v[16], v[17]), pack(v[18], v[19]), pack(v[20], v[21]), pack(v[22], v[23])};
     }
     if (block_any(sp.failed, smem)) return false;
   } else {
