@@ -506,9 +506,11 @@ struct FmtInt4 {
 // RMSNorm with bf16 gain -> optional bf16 rounding -> LDS in the chunk
 // layout of format F; int8 also gets sum x, int4 the per-chunk sums of x.
 // n is a multiple of 8.  False when a tagged read gave up.
-template <class F, bool SRC_BF16, bool NORM>
+template <class F>
 __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, const uint64_t* tsrc, int n,
-                                        const uint16_t* gain, float* xs, float* red, float* xsum, float* csum) {
+                                        const uint16_t* gain, bool src_bf16, float* xs, float* red, float* xsum,
+                                        float* csum) {
+  const bool NORM = gain != nullptr;
   const int tid = opaque_tid(), n4 = n >> 2;
   const float eps = P.eps;
   const int act_bf16 = P.act_bf16;
@@ -534,7 +536,7 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
   } else
   for (int i = tid; i < n4; i += kThreads) {
     float4 v;
-    if (SRC_BF16) {
+    if (src_bf16) {
       const uint2 b = reinterpret_cast<const uint2*>(src)[i];
       v = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
     } else {
@@ -763,10 +765,10 @@ __device__ __forceinline__ int xs_floats(int K) {
 // (rows_total rows of K inputs) on the input vector `src` (RMSNorm'd with
 // `gain` when NORM), waiting for the task's counters after the first weight
 // loads are issued.  Results: res[i] for i < nunits*RPU (LDS).
-template <int DEPTH, int WFMT, int RPU, bool SRC_BF16, bool NORM>
+template <int DEPTH, int WFMT, int RPU>
 __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* smem, const uint8_t* ptr,
                                         int64_t rows_total, int K, int row0, int nunits, const void* src,
-                                        const uint64_t* tsrc, const uint16_t* gain) {
+                                        const uint64_t* tsrc, const uint16_t* gain, bool src_bf16) {
   using F = typename std::conditional<WFMT == AMK_W_BF16, FmtBf16,
             typename std::conditional<WFMT == AMK_W_INT8_ROW, FmtInt8, FmtInt4>::type>::type;
   float* red = smem;                                  // kWaves floats
@@ -799,7 +801,7 @@ __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* sme
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
       }
     });
-    if (ok) ok = stage_x<F, SRC_BF16, NORM>(P, src, tsrc, K, gain, xs, red, xsum, csum);
+    if (ok) ok = stage_x<F>(P, src, tsrc, K, gain, src_bf16, xs, red, xsum, csum);
     if (ok && P.tagged) trace_mark(P, t, 1);
   });
   if (!ok) return false;
@@ -817,178 +819,166 @@ __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* sme
 
 // ---------------------------------------------------------------- tasks --
 
+// The GEMV tasks (QKV, O, gate/up, down, LM head) share one body: the
+// task's operand choice, one projection (row pairs when the row count is
+// even), then the task's epilogue.  Every GEMV phase runs the same code, so
+// the instruction cache keeps it between phases.
 template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_qkv(const VmParams& P, TaskRef t, float* smem) {
-  const int l = t.p[0], u0 = t.p[1], u1 = t.p[2];
-  const int H = P.H, hd = P.hd, half = hd >> 1, nq = P.nq, nkv = P.nkv;
-  const uint8_t* w = P.wptr[3 + 6 * l + LB_QKV];
-  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_ATTN_NORM]);
-  const int64_t rows = (int64_t)(nq + 2 * nkv) * hd;
-  bool ok;
-  if (l == 0) {
-    const void* src = P.wptr[0] + (int64_t)P.token * H * 2;
-    ok = project<DEPTH, WFMT, 2, true, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, src, nullptr, gain);
-  } else {
-    const int64_t off = ((int64_t)(l - 1) * 2 + 1) * H;
-    ok = project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, rows, H, 2 * u0, u1 - u0, P.x + off,
-                                              P.tagged ? P.tx + off : nullptr, gain);
-  }
-  if (!ok) return false;
-  const float* res = smem + kHead + xs_floats<WFMT>(H);
+__device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* smem) {
+  const int type = t.type;
+  const int H = P.H, F = P.F, hd = P.hd, half = hd >> 1, nq = P.nq, nkv = P.nkv, qd = nq * hd;
+  const int l = type == AMK_TASK_LMHEAD ? P.L - 1 : t.p[0];
   const int tid = opaque_tid();
-  const int EW = epilogue_threads(P);
-  if (tid < EW)
-  for (int k = tid; k < u1 - u0; k += EW) {
-    const int u = u0 + k, hs = u / half, i = u - hs * half;
-    float a = res[2 * k], b = res[2 * k + 1];
-    if (hs < nq + nkv) {
-      const float2 cs = P.rope[(int64_t)P.pos * half + i];
-      const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
-      a = ra;
-      b = rb;
-    }
-    if (hs < nq) {
-      const int64_t qo = (int64_t)l * nq * hd + (int64_t)hs * hd;
-      if (P.tagged) {
-        st_tag(P.tq + qo + i, a, P.tag);
-        st_tag(P.tq + qo + i + half, b, P.tag);
+  const uint8_t* w;
+  const uint16_t* gain = nullptr;
+  const void* src;
+  const uint64_t* tsrc = nullptr;
+  bool src_bf16 = false;
+  int64_t rows_total;
+  int K, row0, nrows;
+  const int64_t xin = ((int64_t)(l - 1) * 2 + 1) * H;  // previous layer's output
+  const int64_t xmid = (int64_t)l * 2 * H, xout = ((int64_t)l * 2 + 1) * H;
+  int64_t resid_off = -1;  // O / down: where the residual rows are read
+  switch (type) {
+    case AMK_TASK_QKV:
+      w = P.wptr[3 + 6 * l + LB_QKV];
+      gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_ATTN_NORM]);
+      rows_total = (int64_t)(nq + 2 * nkv) * hd;
+      K = H;
+      row0 = 2 * t.p[1];
+      nrows = 2 * (t.p[2] - t.p[1]);
+      if (l == 0) {
+        src = P.wptr[0] + (int64_t)P.token * H * 2;
+        src_bf16 = true;
       } else {
-        st_agent(P.q + qo + i, a);
-        st_agent(P.q + qo + i + half, b);
+        src = P.x + xin;
+        if (P.tagged) tsrc = P.tx + xin;
       }
-    } else {
-      const int kvsel = hs < nq + nkv ? 0 : 1, g = hs - nq - kvsel * nkv;
-      uint16_t* row = P.kv + ((((int64_t)l * 2 + kvsel) * nkv + g) * P.mc + P.pos) * hd;
-      const uint32_t ba = bf16_bits(a), bb = bf16_bits(b);
-      st_agent(row + i, (uint16_t)ba);
-      st_agent(row + i + half, (uint16_t)bb);
-      if (P.tagged) {  // this launch's row for the attention tasks, as tagged bf16 values
-        uint64_t* tr = P.tkv + (((int64_t)l * 2 + kvsel) * nkv + g) * hd;
-        st_tag(tr + i, __uint_as_float(ba << 16), P.tag);
-        st_tag(tr + i + half, __uint_as_float(bb << 16), P.tag);
-      }
-    }
+      break;
+    case AMK_TASK_OPROJ:
+      w = P.wptr[3 + 6 * l + LB_O];
+      rows_total = H;
+      K = qd;
+      row0 = t.p[1];
+      nrows = t.p[2] - t.p[1];
+      src = P.o + (int64_t)l * qd;
+      if (P.tagged) tsrc = P.to + (int64_t)l * qd;
+      if (l > 0) resid_off = xin;
+      break;
+    case AMK_TASK_GATEUP:
+      w = P.wptr[3 + 6 * l + LB_GATEUP];
+      gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_MLP_NORM]);
+      rows_total = 2 * (int64_t)F;
+      K = H;
+      row0 = 2 * t.p[1];
+      nrows = 2 * (t.p[2] - t.p[1]);
+      src = P.x + xmid;
+      if (P.tagged) tsrc = P.tx + xmid;
+      break;
+    case AMK_TASK_DOWN:
+      w = P.wptr[3 + 6 * l + LB_DOWN];
+      rows_total = H;
+      K = F;
+      row0 = t.p[1];
+      nrows = t.p[2] - t.p[1];
+      src = P.a + (int64_t)l * F;
+      if (P.a_tagged) tsrc = P.ta + (int64_t)l * F;
+      resid_off = xmid;
+      break;
+    default:  // AMK_TASK_LMHEAD
+      w = P.wptr[2];
+      gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
+      rows_total = P.V;
+      K = H;
+      row0 = t.p[0];
+      nrows = t.p[1] - t.p[0];
+      src = P.x + xout;
+      if (P.tagged) tsrc = P.tx + xout;
+      break;
   }
-  vm_signal(P, t);
-  return true;
-}
-
-template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_oproj(const VmParams& P, TaskRef t, float* smem) {
-  const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
-  const int H = P.H, qd = P.nq * P.hd;
-  const uint8_t* w = P.wptr[3 + 6 * l + LB_O];
-  const float* src = P.o + (int64_t)l * qd;
-  const uint64_t* tsrc = P.tagged ? P.to + (int64_t)l * qd : nullptr;
-  const int64_t dst = (int64_t)l * 2 * H, prev = ((int64_t)(l - 1) * 2 + 1) * H;
   // tagged: the first residual row of each thread, read before the weight
-  // stream so that it is not queued behind it (the previous layer's output,
-  // complete once this queue's own QKV task staged it; checked anyway)
+  // stream so that it is not queued behind it (written by an earlier phase
+  // whose output this queue's previous GEMV task staged in full; checked
+  // anyway)
   uint64_t rres = 0;
-  if (P.tagged && l > 0 && opaque_tid() < r1 - r0) rres = ld_tag(P.tx + prev + r0 + opaque_tid());
-  // rows go in pairs when the count is even (two loads per step), else singly
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, qd, r0, r1 - r0, src, tsrc, nullptr)
-                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, qd, r0, (r1 - r0) / 2, src, tsrc, nullptr);
+  if (P.tagged && resid_off >= 0 && tid < nrows) rres = ld_tag(P.tx + resid_off + t.p[1] + tid);
+  const bool ok = nrows & 1 ? project<DEPTH, WFMT, 1>(P, t, smem, w, rows_total, K, row0, nrows, src, tsrc, gain, src_bf16)
+                            : project<DEPTH, WFMT, 2>(P, t, smem, w, rows_total, K, row0, nrows / 2, src, tsrc, gain,
+                                                      src_bf16);
   if (!ok) return false;
-  const float* res = smem + kHead + xs_floats<WFMT>(qd);
-  const int tid = opaque_tid();
+  const float* res = smem + kHead + xs_floats<WFMT>(K);
   const int EW = epilogue_threads(P);
-  if (P.tagged) {  // residual rows of the previous layer's output are tagged words too
-    TagSpin sp;
-    for (int k = tid; k < r1 - r0 && !sp.failed; k += kThreads) {
-      const int r = r0 + k;
-      float resid[1];
-      if (l == 0) resid[0] = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
-      else if (k == tid && (uint32_t)(rres >> 32) == P.tag) resid[0] = tag_val(rres);
-      else if (!ld_tagged<1>(P, P.tx + prev, [](int) { return true; }, [&](int) { return r; }, resid, sp)) break;
-      st_tag(P.tx + dst + r, resid[0] + res[k], P.tag);
+  if (type == AMK_TASK_QKV) {
+    const int u0 = t.p[1], u1 = t.p[2];
+    if (tid < EW)
+      for (int k = tid; k < u1 - u0; k += EW) {
+        const int u = u0 + k, hs = u / half, i = u - hs * half;
+        float a = res[2 * k], b = res[2 * k + 1];
+        if (hs < nq + nkv) {
+          const float2 cs = P.rope[(int64_t)P.pos * half + i];
+          const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
+          a = ra;
+          b = rb;
+        }
+        if (hs < nq) {
+          const int64_t qo = (int64_t)l * nq * hd + (int64_t)hs * hd;
+          if (P.tagged) {
+            st_tag(P.tq + qo + i, a, P.tag);
+            st_tag(P.tq + qo + i + half, b, P.tag);
+          } else {
+            st_agent(P.q + qo + i, a);
+            st_agent(P.q + qo + i + half, b);
+          }
+        } else {
+          const int kvsel = hs < nq + nkv ? 0 : 1, g = hs - nq - kvsel * nkv;
+          uint16_t* row = P.kv + ((((int64_t)l * 2 + kvsel) * nkv + g) * P.mc + P.pos) * hd;
+          const uint32_t ba = bf16_bits(a), bb = bf16_bits(b);
+          st_agent(row + i, (uint16_t)ba);
+          st_agent(row + i + half, (uint16_t)bb);
+          if (P.tagged) {  // this launch's row for the attention tasks, as tagged bf16 values
+            uint64_t* tr = P.tkv + (((int64_t)l * 2 + kvsel) * nkv + g) * hd;
+            st_tag(tr + i, __uint_as_float(ba << 16), P.tag);
+            st_tag(tr + i + half, __uint_as_float(bb << 16), P.tag);
+          }
+        }
+      }
+  } else if (type == AMK_TASK_OPROJ || type == AMK_TASK_DOWN) {
+    // residual add: O adds the previous layer's output (the embedding row at
+    // layer 0), down adds this layer's attention output
+    const int r0 = t.p[1];
+    const int64_t dst = type == AMK_TASK_OPROJ ? xmid : xout;
+    if (P.tagged) {
+      TagSpin sp;
+      for (int k = tid; k < nrows && !sp.failed; k += kThreads) {
+        const int r = r0 + k;
+        float resid[1];
+        if (resid_off < 0) resid[0] = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
+        else if (k == tid && (uint32_t)(rres >> 32) == P.tag) resid[0] = tag_val(rres);
+        else if (!ld_tagged<1>(P, P.tx + resid_off, [](int) { return true; }, [&](int) { return r; }, resid, sp)) break;
+        st_tag(P.tx + dst + r, resid[0] + res[k], P.tag);
+      }
+      if (block_any(sp.failed, smem)) return false;
+    } else if (tid < EW) {
+      for (int k = tid; k < nrows; k += EW) {
+        const int r = r0 + k;
+        const float resid = resid_off < 0 ? bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r])
+                                          : P.x[resid_off + r];
+        st_agent(P.x + dst + r, resid + res[k]);
+      }
     }
-    if (block_any(sp.failed, smem)) return false;
-  } else if (tid < EW)
-  for (int k = tid; k < r1 - r0; k += EW) {
-    const int r = r0 + k;
-    float resid;
-    if (l == 0) resid = bf16_to_f(reinterpret_cast<const uint16_t*>(P.wptr[0])[(int64_t)P.token * H + r]);
-    else resid = P.x[prev + r];
-    st_agent(P.x + dst + r, resid + res[k]);
+  } else if (type == AMK_TASK_GATEUP) {
+    const int j0 = t.p[1], nj = t.p[2] - t.p[1];
+    const int EWa = P.a_tagged ? kThreads : EW;
+    if (tid < EWa)
+      for (int k = tid; k < nj; k += EWa) {
+        const float g = res[2 * k], u = res[2 * k + 1];
+        const float h = g / (1.0f + expf(-g)) * u;
+        if (P.a_tagged) st_tag(P.ta + (int64_t)l * F + j0 + k, h, P.tag);
+        else st_agent(P.a + (int64_t)l * F + j0 + k, h);
+      }
+  } else {
+    for (int k = tid; k < nrows; k += kThreads) P.logits[row0 + k] = res[k];
   }
-  vm_signal(P, t);
-  return true;
-}
-
-template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_gateup(const VmParams& P, TaskRef t, float* smem) {
-  const int l = t.p[0], j0 = t.p[1], j1 = t.p[2];
-  const int H = P.H, F = P.F;
-  const uint8_t* w = P.wptr[3 + 6 * l + LB_GATEUP];
-  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[3 + 6 * l + LB_MLP_NORM]);
-  const float* src = P.x + (int64_t)l * 2 * H;
-  const uint64_t* tsrc = P.tagged ? P.tx + (int64_t)l * 2 * H : nullptr;
-  if (!project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, 2 * (int64_t)F, H, 2 * j0, j1 - j0, src, tsrc, gain))
-    return false;
-  const float* res = smem + kHead + xs_floats<WFMT>(H);
-  const int64_t dst = (int64_t)l * F;
-  const int tid = opaque_tid();
-  const int EW = P.a_tagged ? kThreads : epilogue_threads(P);
-  if (tid < EW)
-  for (int k = tid; k < j1 - j0; k += EW) {
-    const float g = res[2 * k], u = res[2 * k + 1];
-    const float h = g / (1.0f + expf(-g)) * u;
-    if (P.a_tagged) st_tag(P.ta + dst + j0 + k, h, P.tag);
-    else st_agent(P.a + dst + j0 + k, h);
-  }
-  vm_signal(P, t);
-  return true;
-}
-
-template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_down(const VmParams& P, TaskRef t, float* smem) {
-  const int l = t.p[0], r0 = t.p[1], r1 = t.p[2];
-  const int H = P.H, F = P.F;
-  const uint8_t* w = P.wptr[3 + 6 * l + LB_DOWN];
-  const float* src = P.a + (int64_t)l * F;
-  const uint64_t* tsrc = P.a_tagged ? P.ta + (int64_t)l * F : nullptr;
-  const int64_t mid = (int64_t)l * 2 * H, dst = ((int64_t)l * 2 + 1) * H;
-  // tagged: the first residual row of each thread, read ahead of the weight
-  // stream (this layer's attention output, complete once this queue's own
-  // gate/up task staged it; checked anyway)
-  uint64_t rres = 0;
-  if (P.tagged && opaque_tid() < r1 - r0) rres = ld_tag(P.tx + mid + r0 + opaque_tid());
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, false>(P, t, smem, w, H, F, r0, r1 - r0, src, tsrc, nullptr)
-                                : project<DEPTH, WFMT, 2, false, false>(P, t, smem, w, H, F, r0, (r1 - r0) / 2, src, tsrc, nullptr);
-  if (!ok) return false;
-  const float* res = smem + kHead + xs_floats<WFMT>(F);
-  const int tid = opaque_tid();
-  const int EW = epilogue_threads(P);
-  if (P.tagged) {  // residual rows (this layer's attention output) are tagged words
-    TagSpin sp;
-    for (int k = tid; k < r1 - r0 && !sp.failed; k += kThreads) {
-      float m[1];
-      if (k == tid && (uint32_t)(rres >> 32) == P.tag) m[0] = tag_val(rres);
-      else if (!ld_tagged<1>(P, P.tx + mid, [](int) { return true; }, [&](int) { return r0 + k; }, m, sp)) break;
-      st_tag(P.tx + dst + r0 + k, m[0] + res[k], P.tag);
-    }
-    if (block_any(sp.failed, smem)) return false;
-  } else if (tid < EW)
-    for (int k = tid; k < r1 - r0; k += EW) st_agent(P.x + dst + r0 + k, P.x[mid + r0 + k] + res[k]);
-  vm_signal(P, t);
-  return true;
-}
-
-template <int DEPTH, int WFMT>
-__device__ __forceinline__ bool task_lmhead(const VmParams& P, TaskRef t, float* smem) {
-  const int r0 = t.p[0], r1 = t.p[1];
-  const int H = P.H;
-  const uint8_t* w = P.wptr[2];
-  const uint16_t* gain = reinterpret_cast<const uint16_t*>(P.wptr[1]);
-  const int64_t off = ((int64_t)(P.L - 1) * 2 + 1) * H;
-  const float* src = P.x + off;
-  const uint64_t* tsrc = P.tagged ? P.tx + off : nullptr;
-  const bool ok = (r1 - r0) & 1 ? project<DEPTH, WFMT, 1, false, true>(P, t, smem, w, P.V, H, r0, r1 - r0, src, tsrc, gain)
-                                : project<DEPTH, WFMT, 2, false, true>(P, t, smem, w, P.V, H, r0, (r1 - r0) / 2, src, tsrc, gain);
-  if (!ok) return false;
-  const float* res = smem + kHead + xs_floats<WFMT>(H);
-  for (int k = opaque_tid(); k < r1 - r0; k += kThreads) P.logits[r0 + k] = res[k];
   vm_signal(P, t);
   return true;
 }
@@ -1441,13 +1431,13 @@ __device__ __forceinline__ void issue_prefetch(const VmParams& P, const PfNext& 
 template <int DEPTH, int WFMT>
 __device__ __forceinline__ bool run_task(const VmParams& P, TaskRef t, float* smem) {
   switch (t.type) {
-    case AMK_TASK_QKV: return task_qkv<DEPTH, WFMT>(P, t, smem);
+    case AMK_TASK_QKV:
+    case AMK_TASK_OPROJ:
+    case AMK_TASK_GATEUP:
+    case AMK_TASK_DOWN:
+    case AMK_TASK_LMHEAD: return task_gemv<DEPTH, WFMT>(P, t, smem);
     case AMK_TASK_ATTN: return task_attn(P, t, smem);
     case AMK_TASK_MERGE: return task_merge(P, t, smem);
-    case AMK_TASK_OPROJ: return task_oproj<DEPTH, WFMT>(P, t, smem);
-    case AMK_TASK_GATEUP: return task_gateup<DEPTH, WFMT>(P, t, smem);
-    case AMK_TASK_DOWN: return task_down<DEPTH, WFMT>(P, t, smem);
-    case AMK_TASK_LMHEAD: return task_lmhead<DEPTH, WFMT>(P, t, smem);
     default: return task_nop(P, t, smem);
   }
 }
