@@ -354,6 +354,20 @@ amk_status amk_engine_create(const amk_schedule* schedule, const amk_device_buff
  * rewinds (rows from pos on are overwritten).  One engine per stream. */
 amk_status amk_decode_step(amk_engine* engine, int32_t token, int32_t pos, void* hip_stream);
 
+/* Greedy decoding of n_steps tokens in ONE cooperative launch, the token fed
+ * back on the device (the megakernel page's single kernel that also covers
+ * the logits and sampling, section on the megakernel design): step s
+ * decodes at position pos + s; step 0 consumes `token`, step s > 0 the
+ * argmax of step s - 1's logits (lowest index on ties).  tokens_out is a
+ * DEVICE int32[n_steps] (caller-owned) that receives the argmax of every
+ * step's logits; buffers->logits holds the last step's logits.  Every
+ * workgroup computes the argmax itself from one (max, index) partial per
+ * LM-head task, so no extra join is added.  n_steps < 1 or pos + n_steps >
+ * max_ctx -> AMK_ERR_OUT_OF_RANGE; null tokens_out -> AMK_ERR_INVALID_ARG;
+ * otherwise as amk_decode_step. */
+amk_status amk_decode_steps(amk_engine* engine, int32_t token, int32_t pos, int32_t n_steps,
+                            int32_t* tokens_out, void* hip_stream);
+
 /* Declare that KV-cache rows 0..n_positions-1 already hold valid state the
  * caller wrote (a restored cache, or a prefix filled outside the library), so
  * the next decode step may use any pos <= n_positions.  0 <= n_positions <=
@@ -382,6 +396,23 @@ amk_status amk_engine_set_trace(amk_engine* engine, int32_t enable);
  * 4 * n_tasks; *clock_khz receives the stamp clock rate. */
 amk_status amk_engine_read_trace(amk_engine* engine, uint64_t* out, int64_t n_values,
                                  int32_t* clock_khz);
+
+/* Region timing per task type of the last traced launch (device stamps
+ * aggregated per region, as the Argus page's megakernel case study,
+ * "Case 3", attributes a step's time to its phases).  out[type] for every
+ * amk_task_type: tasks of that type, and over them the summed microseconds
+ * from wait begin to inputs in hand (wait), to work end (work) and to signal
+ * end (signal); span_us sums, over the layers, the time from the last signal
+ * of the phase before it in the layer's order (QKV, ATTN, MERGE, OPROJ,
+ * GATEUP, DOWN; the previous layer's DOWN before QKV, the launch start
+ * before layer 0) to the type's own last signal, so the spans of all types
+ * add up to the traced launch's length: each type's share of the critical
+ * path.  AMK_ERR_INVALID_ARG if tracing was never enabled. */
+typedef struct {
+  int32_t n_tasks;
+  double wait_us, work_us, signal_us, span_us;
+} amk_region_stat;
+amk_status amk_engine_region_stats(amk_engine* engine, amk_region_stat out[AMK_TASK_NTYPES]);
 
 /* Host-side count of decode steps since creation (for the caller's bookkeeping). */
 amk_status amk_engine_steps(const amk_engine* engine, int64_t* out);

@@ -66,6 +66,15 @@ class ScheduleConfig(ctypes.Structure):
                 for n, _ in self._fields_}
 
 
+TASK_NAMES = ["NOP", "QKV", "ATTN", "MERGE", "OPROJ", "GATEUP", "DOWN", "LMHEAD"]
+TASK_NTYPES = len(TASK_NAMES)
+
+
+class RegionStat(ctypes.Structure):
+    _fields_ = [("n_tasks", _i32), ("wait_us", ctypes.c_double), ("work_us", ctypes.c_double),
+                ("signal_us", ctypes.c_double), ("span_us", ctypes.c_double)]
+
+
 class TaskDesc(ctypes.Structure):
     _fields_ = [("type", _i32), ("cu", _i32), ("p", _i32 * 8)]
 
@@ -119,11 +128,13 @@ _SIGS = {
     "amk_kv_bytes": ([ctypes.POINTER(ModelConfig), ctypes.POINTER(ctypes.c_size_t)], _i32),
     "amk_engine_create": ([_p, ctypes.POINTER(DeviceBuffers), ctypes.POINTER(_p)], _i32),
     "amk_decode_step": ([_p, _i32, _i32, _p], _i32),
+    "amk_decode_steps": ([_p, _i32, _i32, _i32, _p, _p], _i32),
     "amk_engine_check": ([_p], _i32),
     "amk_engine_set_spin_budget": ([_p, _i64], _i32),
     "amk_engine_set_kv_length": ([_p, _i32], _i32),
     "amk_engine_set_trace": ([_p, _i32], _i32),
     "amk_engine_read_trace": ([_p, _p, _i64, ctypes.POINTER(_i32)], _i32),
+    "amk_engine_region_stats": ([_p, _p], _i32),
     "amk_engine_steps": ([_p, ctypes.POINTER(_i64)], _i32),
     "amk_engine_destroy": ([_p], _i32),
     "amk_stream_read_probe": ([_p, ctypes.c_size_t, _p, _i32, _p], _i32),
@@ -388,6 +399,16 @@ class Engine:
         _check(_lib.amk_decode_step(self._h, int(token), int(pos), ctypes.c_void_p(s.cuda_stream)),
                "amk_decode_step")
 
+    def decode_steps(self, token, pos, n_steps, tokens_out, stream=None):
+        """Greedy decode of n_steps tokens in one launch (amk_decode_steps);
+        tokens_out: a device int32 tensor of at least n_steps elements."""
+        import torch
+        assert tokens_out.dtype == torch.int32 and tokens_out.is_cuda and tokens_out.numel() >= n_steps
+        s = stream if stream is not None else torch.cuda.current_stream()
+        _check(_lib.amk_decode_steps(self._h, int(token), int(pos), int(n_steps),
+                                     ctypes.c_void_p(tokens_out.data_ptr()), ctypes.c_void_p(s.cuda_stream)),
+               "amk_decode_steps")
+
     def check(self):
         _check(_lib.amk_engine_check(self._h), "amk_engine_check")
 
@@ -404,6 +425,14 @@ class Engine:
         _check(_lib.amk_engine_read_trace(self._h, out.ctypes.data, out.size, ctypes.byref(khz)),
                "amk_engine_read_trace")
         return out, khz.value
+
+    def region_stats(self):
+        """Per task type of the last traced launch (amk_engine_region_stats):
+        {name: {n_tasks, wait_us, work_us, signal_us, span_us}}."""
+        out = (RegionStat * TASK_NTYPES)()
+        _check(_lib.amk_engine_region_stats(self._h, ctypes.cast(out, _p)), "amk_engine_region_stats")
+        return {TASK_NAMES[k]: {f: getattr(out[k], f) for f, _ in RegionStat._fields_}
+                for k in range(TASK_NTYPES) if out[k].n_tasks}
 
     def set_spin_budget(self, microseconds):
         _check(_lib.amk_engine_set_spin_budget(self._h, int(microseconds)), "amk_engine_set_spin_budget")

@@ -83,6 +83,14 @@ struct VmParams {
   uint64_t* tpart; // [L][nq][S][hd+2] as part
   uint64_t* to;    // [L][nq*hd] as o
   uint64_t* ta;    // [L][F] as a
+  // greedy multi-step decode: n_steps steps in one launch; step s decodes at
+  // pos + s with tag + s and epoch + s, its token being the argmax of step
+  // s - 1's logits.  LM-head task k stores its rows' (max, index) as two
+  // tagged words targ[2k], targ[2k + 1] (its ordinal k is its p[2]).
+  int32_t n_steps;
+  int32_t n_lm;
+  uint64_t* targ;        // [n_lm][2]
+  int32_t* tokens_out;   // device int32[n_steps] or null: every step's argmax
 };
 
 // ------------------------------------------------------------- helpers --
@@ -191,6 +199,37 @@ __device__ __forceinline__ bool block_any(bool pred, float* red) {
   for (int k = 0; k < kWaves; ++k) any |= reinterpret_cast<const int*>(red)[k];
   __syncthreads();
   return any != 0;
+}
+
+// (best, index) over the workgroup: the largest value, the lowest index among
+// equal values; the result is in thread 0.  Uses the first 2*kWaves floats
+// of `red`.
+__device__ __forceinline__ void argmax_block(float& best, int& bi, float* red) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ob > best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  __syncthreads();
+  const int tid = opaque_tid();
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = best;
+    reinterpret_cast<int*>(red)[kWaves + (tid >> 6)] = bi;
+  }
+  __syncthreads();
+  if (tid == 0)
+    for (int w = 1; w < kWaves; ++w) {
+      const float ob = red[w];
+      const int oi = reinterpret_cast<const int*>(red)[kWaves + w];
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+  __syncthreads();
 }
 
 // relaxed agent-scope load: a vector load that no cache level keeps stale
@@ -977,7 +1016,24 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
         else st_agent(P.a + (int64_t)l * F + j0 + k, h);
       }
   } else {
-    for (int k = tid; k < nrows; k += kThreads) P.logits[row0 + k] = res[k];
+    // logits, and this task's (max, lowest index of the max) for the greedy
+    // token of the next step
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int k = tid; k < nrows; k += kThreads) {
+      P.logits[row0 + k] = res[k];
+      if (res[k] > best) {
+        best = res[k];
+        bi = row0 + k;
+      }
+    }
+    if (P.tokens_out) {  // a multi-step launch: the partial feeds the next token
+      argmax_block(best, bi, smem);
+      if (tid == 0) {
+        st_tag(P.targ + 2 * t.p[2], best, P.tag);
+        st_tag(P.targ + 2 * t.p[2] + 1, __int_as_float(bi), P.tag);
+      }
+    }
   }
   vm_signal(P, t);
   return true;
@@ -1451,16 +1507,70 @@ __device__ __forceinline__ bool run_one(const VmParams& P, TaskRef t, float* sme
 }
 
 
+// Argmax of the last step's logits from the LM-head tasks' tagged (max,
+// index) partials, lowest index on ties; the same value in every thread.
+__device__ __forceinline__ bool greedy_token(const VmParams& P, float* smem, int* tok) {
+  const int tid = opaque_tid();
+  TagSpin sp;
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int k = tid; k < P.n_lm && !sp.failed; k += kThreads) {
+    float v[2];
+    if (!ld_tagged<2>(P, P.targ + 2 * k, [](int) { return true; }, [](int j) { return j; }, v, sp)) break;
+    const int i = __float_as_int(v[1]);
+    if (v[0] > best || (v[0] == best && i < bi)) {
+      best = v[0];
+      bi = i;
+    }
+  }
+  if (block_any(sp.failed, smem)) return false;
+  argmax_block(best, bi, smem);
+  if (bi < 0 || bi >= P.V) bi = 0;  // all logits NaN: keep the embedding gather in range
+  if (tid == 0) reinterpret_cast<int*>(smem)[0] = bi;
+  __syncthreads();
+  *tok = reinterpret_cast<const int*>(smem)[0];
+  __syncthreads();
+  return true;
+}
+
 // Workgroup b walks queue b in order.  A task that fails its wait (spin
 // budget spent, or another workgroup reported an error) ends the walk; the
 // error word tells every other workgroup to stop at its next wait.
-template <int DEPTH, int WFMT>
-__global__ void __launch_bounds__(kThreads) amk_vm(VmParams P) {
+template <int DEPTH, int WFMT, bool MULTI>
+__global__ void __launch_bounds__(kThreads) amk_vm(VmParams P0) {
   extern __shared__ __align__(16) float smem[];
-  const int q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
-  for (int qi = q0; qi < q1; ++qi) {
-    const int ti = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)P.queue)[qi];
-    if (!run_one<DEPTH, WFMT>(P, ((CTask*)(uintptr_t)P.tasks)[ti], smem)) return;
+  const int q0 = P0.queue_off[blockIdx.x], q1 = P0.queue_off[blockIdx.x + 1];
+  if constexpr (!MULTI) {  // one step: the parameters stay in the kernel-argument segment
+    for (int qi = q0; qi < q1; ++qi) {
+      const int ti = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)P0.queue)[qi];
+      if (!run_one<DEPTH, WFMT>(P0, ((CTask*)(uintptr_t)P0.tasks)[ti], smem)) return;
+    }
+    return;
+  }
+  VmParams P = P0;
+  for (int s = 0; s < P0.n_steps; ++s) {
+    if (s > 0) {
+      // the next token: argmax over the LM-head tasks' partials of step s - 1
+      // (every workgroup computes it); then an acquire, so that plain loads
+      // of KV rows written in step s - 1 by other workgroups see them
+      int tok;
+      if (!greedy_token(P, smem, &tok)) return;
+      if (blockIdx.x == 0 && opaque_tid() == 0 && P.tokens_out) P.tokens_out[s - 1] = tok;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      P.token = tok;
+      P.pos += 1;
+      P.tag += 1;
+      P.epoch += 1;
+    }
+    for (int qi = q0; qi < q1; ++qi) {
+      const int ti = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)P.queue)[qi];
+      if (!run_one<DEPTH, WFMT>(P, ((CTask*)(uintptr_t)P.tasks)[ti], smem)) return;
+    }
+  }
+  if (blockIdx.x == 0 && P.tokens_out) {  // the last step's token
+    int tok;
+    if (!greedy_token(P, smem, &tok)) return;
+    if (opaque_tid() == 0) P.tokens_out[P0.n_steps - 1] = tok;
   }
 }
 
@@ -1487,15 +1597,24 @@ __global__ void __launch_bounds__(256) amk_stream_read(const uint4* __restrict__
   if (acc == 0x9E3779B9u) out[blockIdx.x] = 1.0f;
 }
 
-template __global__ void amk_vm<4, AMK_W_BF16>(VmParams);
-template __global__ void amk_vm<4, AMK_W_INT8_ROW>(VmParams);
-template __global__ void amk_vm<4, AMK_W_INT4_G128>(VmParams);
-template __global__ void amk_vm<8, AMK_W_BF16>(VmParams);
-template __global__ void amk_vm<8, AMK_W_INT8_ROW>(VmParams);
-template __global__ void amk_vm<8, AMK_W_INT4_G128>(VmParams);
-template __global__ void amk_vm<16, AMK_W_BF16>(VmParams);
-template __global__ void amk_vm<16, AMK_W_INT8_ROW>(VmParams);
-template __global__ void amk_vm<16, AMK_W_INT4_G128>(VmParams);
+template __global__ void amk_vm<4, AMK_W_BF16, false>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT8_ROW, false>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT4_G128, false>(VmParams);
+template __global__ void amk_vm<8, AMK_W_BF16, false>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT8_ROW, false>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT4_G128, false>(VmParams);
+template __global__ void amk_vm<16, AMK_W_BF16, false>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT8_ROW, false>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT4_G128, false>(VmParams);
+template __global__ void amk_vm<4, AMK_W_BF16, true>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT8_ROW, true>(VmParams);
+template __global__ void amk_vm<4, AMK_W_INT4_G128, true>(VmParams);
+template __global__ void amk_vm<8, AMK_W_BF16, true>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT8_ROW, true>(VmParams);
+template __global__ void amk_vm<8, AMK_W_INT4_G128, true>(VmParams);
+template __global__ void amk_vm<16, AMK_W_BF16, true>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT8_ROW, true>(VmParams);
+template __global__ void amk_vm<16, AMK_W_INT4_G128, true>(VmParams);
 
 }  // namespace amk
 
@@ -1509,20 +1628,22 @@ namespace {
     if (e_ != hipSuccess) return fail(AMK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
-template <int D>
+template <int D, bool M>
 const void* kernel_for_format(int wfmt) {
   switch (wfmt) {
-    case AMK_W_INT8_ROW: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT8_ROW>);
-    case AMK_W_INT4_G128: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT4_G128>);
-    default: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_BF16>);
+    case AMK_W_INT8_ROW: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT8_ROW, M>);
+    case AMK_W_INT4_G128: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_INT4_G128, M>);
+    default: return reinterpret_cast<const void*>(&amk_vm<D, AMK_W_BF16, M>);
   }
 }
 
+// the single-step kernel (M = false) or the greedy multi-step one
+template <bool M>
 const void* kernel_for(int depth, int wfmt) {
   switch (depth) {
-    case 4: return kernel_for_format<4>(wfmt);
-    case 8: return kernel_for_format<8>(wfmt);
-    default: return kernel_for_format<16>(wfmt);
+    case 4: return kernel_for_format<4, M>(wfmt);
+    case 8: return kernel_for_format<8, M>(wfmt);
+    default: return kernel_for_format<16, M>(wfmt);
   }
 }
 
@@ -1533,7 +1654,8 @@ struct amk_engine {
   amk_model_config model{};
   amk_schedule_config config{};
   int device = 0;
-  const void* kernel = nullptr;
+  const void* kernel = nullptr;        // one decode step per launch
+  const void* kernel_multi = nullptr;  // greedy steps with on-device token feedback
   size_t lds_bytes = 0;
   amk::VmParams params{};
   // device allocations owned by the engine
@@ -1544,6 +1666,7 @@ struct amk_engine {
   int64_t steps = 0;
   int wallclock_khz = 100000;
   int32_t n_tasks = 0;
+  std::vector<int32_t> task_type, task_layer;  // host copies for the region statistics
   uint64_t* d_trace = nullptr;  // allocated on first amk_engine_set_trace(e, 1)
   // tagged activations: one arena, zeroed at creation (tag 0 is never a launch's)
   uint64_t* tag_arena = nullptr;
@@ -1656,6 +1779,50 @@ amk_status check_executable(const amk_schedule& s) {
 
 using namespace amk;
 
+namespace amk {
+namespace {
+
+// One cooperative launch of n steps starting at (token, pos).
+amk_status launch_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n, int32_t* tokens_out, void* stream) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  if (token < 0 || token >= e->model.vocab) return fail(AMK_ERR_OUT_OF_RANGE, "token out of range");
+  if (pos < 0 || pos >= e->model.max_ctx) return fail(AMK_ERR_OUT_OF_RANGE, "pos out of range");
+  if (n < 1 || (int64_t)pos + n > e->model.max_ctx)
+    return fail(AMK_ERR_OUT_OF_RANGE, "steps must be >= 1 and end within max_ctx");
+  if (pos > e->written)
+    return fail(AMK_ERR_INVALID_ARG, "pos " + std::to_string(pos) + " leaves a gap: only " +
+                                         std::to_string(e->written) + " positions are written");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // counters are monotonic across launches; restart them well before u32 wraps
+  if ((uint64_t)(e->params.epoch + n + 2) * e->max_prod >= (1ull << 31)) {
+    HIP_TRY(hipMemsetAsync(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
+    e->params.epoch = 0;
+  }
+  // a launch's tags are never reused while words of an earlier launch may
+  // hold them: near the wrap the tagged words are cleared and tags start
+  // again from 1
+  if ((uint64_t)e->params.tag + (uint64_t)n >= 0xFFFFFFFFull) {
+    if (e->tag_arena) HIP_TRY(hipMemsetAsync(e->tag_arena, 0, e->tag_arena_words * sizeof(uint64_t), st));
+    HIP_TRY(hipMemsetAsync(e->params.targ, 0, sizeof(uint64_t) * 2 * std::max(1, e->params.n_lm), st));
+    e->params.tag = 1;
+  }
+  e->params.token = token;
+  e->params.pos = pos;
+  e->params.n_steps = n;
+  e->params.tokens_out = tokens_out;
+  void* args[] = {&e->params};
+  HIP_TRY(hipLaunchCooperativeKernel(tokens_out ? e->kernel_multi : e->kernel, dim3(e->config.num_cus), dim3(kThreads), args,
+                                     (unsigned)e->lds_bytes, st));
+  e->params.epoch += (uint32_t)n;
+  e->params.tag += (uint32_t)n;
+  e->written = (int64_t)pos + n;
+  e->steps += n;
+  return AMK_OK;
+}
+
+}  // namespace
+}  // namespace amk
+
 extern "C" {
 
 amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out) {
@@ -1723,18 +1890,21 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     return (free_engine(e), fail(AMK_ERR_UNSUPPORTED, "schedule needs " + std::to_string(e->lds_bytes) +
                                                           " bytes of LDS per workgroup; device allows " +
                                                           std::to_string(prop.sharedMemPerBlock)));
-  e->kernel = kernel_for(c.pipeline_depth, m.wfmt);
-  if (e->lds_bytes > 65536) {
-    hipError_t err = hipFuncSetAttribute(e->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds_bytes);
-    if (err != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(err)));
+  e->kernel = kernel_for<false>(c.pipeline_depth, m.wfmt);
+  e->kernel_multi = kernel_for<true>(c.pipeline_depth, m.wfmt);
+  for (const void* k : {e->kernel, e->kernel_multi}) {
+    if (e->lds_bytes > 65536) {
+      hipError_t err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds_bytes);
+      if (err != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(err)));
+    }
+    int per_cu = 0;
+    hipError_t oerr = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, e->lds_bytes);
+    if (oerr != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(oerr)));
+    if ((int64_t)per_cu * prop.multiProcessorCount < c.num_cus)
+      return bail(fail(AMK_ERR_UNSUPPORTED, std::to_string(c.num_cus) + " queues exceed the " +
+                                                std::to_string(per_cu * prop.multiProcessorCount) +
+                                                " co-resident workgroups of this device"));
   }
-  int per_cu = 0;
-  hipError_t oerr = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, e->kernel, kThreads, e->lds_bytes);
-  if (oerr != hipSuccess) return bail(fail(AMK_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(oerr)));
-  if ((int64_t)per_cu * prop.multiProcessorCount < c.num_cus)
-    return bail(fail(AMK_ERR_UNSUPPORTED, std::to_string(c.num_cus) + " queues exceed the " +
-                                              std::to_string(per_cu * prop.multiProcessorCount) +
-                                              " co-resident workgroups of this device"));
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     e->wallclock_khz = khz;
@@ -1745,7 +1915,14 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   for (uint32_t p : P) e->max_prod = std::max(e->max_prod, p);
   e->n_counters = std::max(1, s->n_counters);
   e->n_tasks = (int32_t)s->tasks.size();
+  e->task_type.resize(s->tasks.size());
+  e->task_layer.resize(s->tasks.size());
+  for (size_t i = 0; i < s->tasks.size(); ++i) {
+    e->task_type[i] = s->tasks[i].type;
+    e->task_layer[i] = s->tasks[i].type == AMK_TASK_LMHEAD ? m.n_layers : s->tasks[i].p[0];
+  }
   std::vector<DevTask> dt(s->tasks.size());
+  int32_t n_lm = 0;
   for (size_t i = 0; i < s->tasks.size(); ++i) {
     const Task& t = s->tasks[i];
     DevTask d{};
@@ -1761,6 +1938,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
       d.wprod[k] = P[t.waits[k].ctr];
     }
     for (size_t k = 0; k < t.sigs.size(); ++k) d.sctr[k] = t.sigs[k];
+    if (t.type == AMK_TASK_LMHEAD) d.p[2] = n_lm++;  // slot of its argmax partial
     dt[i] = d;
   }
   for (const auto& q : s->queues)
@@ -1843,6 +2021,10 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   pr.tagged = c.sync_mode != 0;
   pr.a_tagged = c.sync_mode == 1;
   pr.tag = 1;
+  pr.n_steps = 1;
+  pr.n_lm = n_lm;
+  pr.tokens_out = nullptr;
+  if ((st = dev_alloc(e, &pr.targ, (size_t)std::max(1, n_lm) * 2)) != AMK_OK) return bail(st);
   if (pr.tagged) {
     const int64_t nkvd = (int64_t)m.n_kv_heads * hd;
     size_t n = 0;
@@ -1890,34 +2072,13 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
 }
 
 amk_status amk_decode_step(amk_engine* e, int32_t token, int32_t pos, void* stream) {
-  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
-  if (token < 0 || token >= e->model.vocab) return fail(AMK_ERR_OUT_OF_RANGE, "token out of range");
-  if (pos < 0 || pos >= e->model.max_ctx) return fail(AMK_ERR_OUT_OF_RANGE, "pos out of range");
-  if (pos > e->written)
-    return fail(AMK_ERR_INVALID_ARG, "pos " + std::to_string(pos) + " leaves a gap: only " +
-                                         std::to_string(e->written) + " positions are written");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // counters are monotonic across launches; restart them well before u32 wraps
-  if ((uint64_t)(e->params.epoch + 2) * e->max_prod >= (1ull << 31)) {
-    HIP_TRY(hipMemsetAsync(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
-    e->params.epoch = 0;
-  }
-  // a launch's tag is never reused while words of an earlier launch may hold
-  // it: at the wrap the arena is cleared and tags start again from 1
-  if (e->params.tagged && e->params.tag == 0xFFFFFFFFu) {
-    HIP_TRY(hipMemsetAsync(e->tag_arena, 0, e->tag_arena_words * sizeof(uint64_t), st));
-    e->params.tag = 1;
-  }
-  e->params.token = token;
-  e->params.pos = pos;
-  void* args[] = {&e->params};
-  HIP_TRY(hipLaunchCooperativeKernel(e->kernel, dim3(e->config.num_cus), dim3(kThreads), args,
-                                     (unsigned)e->lds_bytes, st));
-  e->params.epoch += 1;
-  e->params.tag += 1;
-  e->written = (int64_t)pos + 1;
-  e->steps += 1;
-  return AMK_OK;
+  return amk::launch_steps(e, token, pos, 1, nullptr, stream);
+}
+
+amk_status amk_decode_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n_steps, int32_t* tokens_out,
+                            void* stream) {
+  if (!tokens_out) return fail(AMK_ERR_INVALID_ARG, "null tokens_out");
+  return amk::launch_steps(e, token, pos, n_steps, tokens_out, stream);
 }
 
 amk_status amk_engine_check(amk_engine* e) {
@@ -1957,6 +2118,49 @@ amk_status amk_engine_read_trace(amk_engine* e, uint64_t* out, int64_t n_values,
   if (n_values != (int64_t)e->n_tasks * 4) return fail(AMK_ERR_INVALID_ARG, "need 4 values per task");
   HIP_TRY(hipMemcpy(out, e->d_trace, sizeof(uint64_t) * n_values, hipMemcpyDeviceToHost));
   if (clock_khz) *clock_khz = e->wallclock_khz;
+  return AMK_OK;
+}
+
+amk_status amk_engine_region_stats(amk_engine* e, amk_region_stat* out) {
+  if (!e || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  if (!e->d_trace) return fail(AMK_ERR_INVALID_ARG, "tracing was never enabled");
+  const size_t n = (size_t)e->n_tasks;
+  std::vector<uint64_t> st(4 * n);
+  HIP_TRY(hipMemcpy(st.data(), e->d_trace, sizeof(uint64_t) * st.size(), hipMemcpyDeviceToHost));
+  const double us = 1e3 / (double)e->wallclock_khz;
+  for (int k = 0; k < AMK_TASK_NTYPES; ++k) out[k] = amk_region_stat{};
+  uint64_t t0 = UINT64_MAX;
+  for (size_t i = 0; i < n; ++i) t0 = std::min(t0, st[4 * i]);
+  // the phases of a layer in dependency order; a phase's span runs from the
+  // last signal of the phase before it (or the launch start) to its own
+  static const int32_t order[] = {AMK_TASK_QKV, AMK_TASK_ATTN, AMK_TASK_MERGE, AMK_TASK_OPROJ, AMK_TASK_GATEUP,
+                                  AMK_TASK_DOWN};
+  const int32_t L = e->model.n_layers;
+  std::vector<uint64_t> last((size_t)(L + 1) * AMK_TASK_NTYPES, 0);
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t ty = e->task_type[i];
+    amk_region_stat& r = out[ty];
+    r.n_tasks += 1;
+    r.wait_us += (double)(st[4 * i + 1] - st[4 * i]) * us;
+    r.work_us += (double)(st[4 * i + 2] - st[4 * i + 1]) * us;
+    r.signal_us += (double)(st[4 * i + 3] - st[4 * i + 2]) * us;
+    uint64_t& l = last[(size_t)e->task_layer[i] * AMK_TASK_NTYPES + ty];
+    l = std::max(l, st[4 * i + 3]);
+  }
+  uint64_t prev = t0;
+  for (int32_t l = 0; l <= L; ++l) {
+    for (int32_t ty : order) {
+      if (l == L) break;
+      const uint64_t end = last[(size_t)l * AMK_TASK_NTYPES + ty];
+      if (end == 0) continue;
+      out[ty].span_us += (double)(std::max(end, prev) - prev) * us;
+      prev = std::max(end, prev);
+    }
+    if (l == L) {
+      const uint64_t end = last[(size_t)L * AMK_TASK_NTYPES + AMK_TASK_LMHEAD];
+      if (end != 0) out[AMK_TASK_LMHEAD].span_us += (double)(std::max(end, prev) - prev) * us;
+    }
+  }
   return AMK_OK;
 }
 

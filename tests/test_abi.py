@@ -151,7 +151,7 @@ def test_default_config_resolves_every_field():
     assert d["num_cus"] == 256 and d["wg_threads"] == 512 and d["pipeline_depth"] in (4, 8, 16)
     assert all(d[k] == 256 for k in ("tiles_qkv", "tiles_o", "tiles_gateup", "tiles_down", "tiles_lm"))
     assert d["attn_splits"] == 3 * 256 // (4 * 8) and d["prefetch_kb"] == 64
-    assert d["sync_mode"] == 1 and d["merge_place"] == 0 and d["prefetch_attn_kb"] == 1024
+    assert d["sync_mode"] == 1 and d["merge_place"] == 0 and d["prefetch_attn_kb"] == 1024 and d["poll_mode"] == 2
 
 
 def test_packed_ids_out_of_range():

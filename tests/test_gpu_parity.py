@@ -98,7 +98,7 @@ def test_full_size_long_context(name, w8b):
 
 
 @pytest.mark.parametrize("sched", [{"prefetch_kb": -1}, {"prefetch_kb": 4}, {"poll_mode": 1},
-                                   {"poll_mode": 2}, {"poll_mode": 2, "pipeline_depth": 16},
+                                   {"poll_mode": 0}, {"poll_mode": 2, "pipeline_depth": 16},
                                    {"poll_mode": 2, "sync_mode": 0},
                                    {"sync_mode": 0}, {"sync_mode": 0, "poll_mode": 1},
                                    {"sync_mode": 0, "release_mode": 1}, {"sync_mode": 0, "attn_splits": 3},
