@@ -338,9 +338,11 @@ def main():
         view = sched.view()
         stamps, khz = eng.read_trace(len(view["tasks"]))
         tr = analyse_trace(view, stamps, khz)
+        tr["regions"] = eng.region_stats()  # per task type, from the library (amk_engine_region_stats)
         with open(args.trace, "w") as f:
             json.dump(tr, f, indent=1)
         out["trace"] = {k: tr[k] for k in ("span_us", "wait_share", "join_latency_us")}
+        out["trace"]["critical_path_us"] = {k: round(v["span_us"], 1) for k, v in tr["regions"].items()}
         log(f"trace: {json.dumps(tr)}")
     del eng
     if not args.no_cpu_baseline:
