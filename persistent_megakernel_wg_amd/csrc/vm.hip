@@ -564,6 +564,13 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
   const float eps = P.eps;
   const int act_bf16 = P.act_bf16;
   float ss = 0.0f;
+  // the gain of this thread's first two groups, read now so that its round
+  // trip overlaps the input's
+  uint2 g2[2] = {{0u, 0u}, {0u, 0u}};
+  if (NORM)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (tid + k * kThreads < n4) g2[k] = reinterpret_cast<const uint2*>(gain)[tid + k * kThreads];
   if (tsrc) {  // up to 4 groups of 4 words per thread in flight at once
     TagSpin sp;
     for (int i0 = tid; i0 < n4; i0 += kThreads * 4) {
@@ -606,7 +613,7 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
     float4* p = reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4));
     float4 v = *p;
     if (NORM) {
-      const uint2 g = reinterpret_cast<const uint2*>(gain)[i];
+      const uint2 g = i == tid ? g2[0] : (i == tid + kThreads ? g2[1] : reinterpret_cast<const uint2*>(gain)[i]);
       v.x = v.x * inv * bf16_lo(g.x);
       v.y = v.y * inv * bf16_hi(g.x);
       v.z = v.z * inv * bf16_lo(g.y);
@@ -958,6 +965,12 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
   // anyway)
   uint64_t rres = 0;
   if (P.tagged && resid_off >= 0 && tid < nrows) rres = ld_tag(P.tx + resid_off + t.p[1] + tid);
+  // QKV: the RoPE (cos, sin) of this thread's first pair unit, read now for the same reason
+  float2 cs0 = make_float2(1.0f, 0.0f);
+  if (type == AMK_TASK_QKV && tid < t.p[2] - t.p[1]) {
+    const int u = t.p[1] + tid, hs = u / half;
+    if (hs < nq + nkv) cs0 = P.rope[(int64_t)P.pos * half + (u - hs * half)];
+  }
   const bool ok = nrows & 1 ? project<DEPTH, WFMT, 1>(P, t, smem, w, rows_total, K, row0, nrows, src, tsrc, gain, src_bf16)
                             : project<DEPTH, WFMT, 2>(P, t, smem, w, rows_total, K, row0, nrows / 2, src, tsrc, gain,
                                                       src_bf16);
@@ -971,7 +984,7 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
         const int u = u0 + k, hs = u / half, i = u - hs * half;
         float a = res[2 * k], b = res[2 * k + 1];
         if (hs < nq + nkv) {
-          const float2 cs = P.rope[(int64_t)P.pos * half + i];
+          const float2 cs = k == tid ? cs0 : P.rope[(int64_t)P.pos * half + i];
           const float ra = a * cs.x - b * cs.y, rb = b * cs.x + a * cs.y;
           a = ra;
           b = rb;
