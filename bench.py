@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--trace", default="", help="after timing, trace 2 steps and write the analysis here")
     ap.add_argument("--prompt-kv", choices=("decode", "synthetic"), default="decode")
     ap.add_argument("--probe", choices=("", "copy"), default="")
+    ap.add_argument("--multistep", action="store_true",
+                    help="also time the same positions as one greedy multi-step launch")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
     if args.traffic_from:
@@ -328,6 +330,24 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if args.multistep:
+        # the same positions decoded greedily in ONE launch (amk_decode_steps):
+        # the token of every step is fed back on the device
+        out_tok = torch.zeros(steps, dtype=torch.int32, device=dev)
+        eng.decode_steps(int(dec[0]), P, steps, out_tok, stream)  # warm-up launch
+        torch.cuda.synchronize()
+        eng.check()
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        eng.decode_steps(int(dec[0]), P, steps, out_tok, stream)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        eng.check()
+        ms = m0.elapsed_time(m1)
+        out["multistep"] = {"launches": 1, "steps": steps, "ms_per_step": ms / steps,
+                            "tokens_per_s": steps / (ms * 1e-3),
+                            "floor_fraction": float(tmin.sum() / (ms * 1e-3))}
+        log(f"multistep: {steps} greedy steps in one launch, {ms / steps:.4f} ms/step")
     if args.trace:
         eng.set_trace(True)
         for i in range(2):
