@@ -330,6 +330,22 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    # the fraction of a plain streaming read's rate on the same device: a
+    # grid-stride read of the largest weight tensor (amk_stream_read_probe)
+    big = max(dev_w, key=lambda x: x.numel() * x.element_size())
+    probe_out = torch.zeros(65536, device=dev)
+    rates = []
+    for blocks in (2048, 8192):
+        amk.stream_read_probe(big, probe_out, blocks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            amk.stream_read_probe(big, probe_out, blocks, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(big.numel() * big.element_size() * 5 / (e0.elapsed_time(e1) * 1e-3))
+    out["stream_read"] = {"GBps": max(rates) / 1e9, "bytes": int(big.numel() * big.element_size()),
+                          "kernel_frac": achieved / max(rates)}
     if args.multistep:
         # the same positions decoded greedily in ONE launch (amk_decode_steps):
         # the token of every step is fed back on the device
