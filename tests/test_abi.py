@@ -246,3 +246,13 @@ def test_sync_mode_limits():
     # the default falls back to counters where the split count is too large
     c = amk.default_schedule_config(amk.ModelConfig.from_workload(synth.get("8b").with_(n_kv_heads=1, n_heads=16)), 256)
     assert c.sync_mode == 0
+
+
+def test_defaults_follow_format_and_context():
+    """Automatic schedule fields: 64 KB prefetch for bf16 weights, none for
+    int8 / int4; 3/4 of the queues run attention splits, all of them past a
+    4096-position cache."""
+    for name, splits, pf in (("8b", 24, 64), ("8b_int8", 24, -1), ("8b_int4", 32, -1), ("1b", 24, 64)):
+        m = amk.ModelConfig.from_workload(synth.get(name))
+        d = amk.default_schedule_config(m, 256).as_dict()
+        assert (d["attn_splits"], d["prefetch_kb"]) == (splits, pf), name
