@@ -103,3 +103,34 @@ def test_multistep_full_size_and_errors():
     for e, s in ((a, sa), (b, sb)):
         e.close()
         s.close()
+
+
+def test_region_stats_account_for_the_traced_launch():
+    """amk_engine_region_stats: task counts per type match the schedule, every
+    duration is non-negative, and the critical-path shares of the types add
+    up to the traced launch's length (first wait begin to last signal)."""
+    import torch
+    wl = synth.get("tiny")
+    w = synth.model_weights(wl, seed=1)
+    eng, sched = _engine(wl, w)
+    with pytest.raises(amk.AmkError):
+        eng.region_stats()  # tracing never enabled
+    eng.set_trace(True)
+    eng.decode_step(3, 0)
+    torch.cuda.synchronize()
+    eng.check()
+    view = sched.view()
+    stats = eng.region_stats()
+    counts = {}
+    for t in view["tasks"]:
+        counts[amk.TASK_NAMES[t["type"]]] = counts.get(amk.TASK_NAMES[t["type"]], 0) + 1
+    assert {k: v["n_tasks"] for k, v in stats.items()} == counts
+    for v in stats.values():
+        assert min(v["wait_us"], v["work_us"], v["signal_us"], v["span_us"]) >= 0.0
+    st, khz = eng.read_trace(len(view["tasks"]))
+    span = (int(st[:, 3].max()) - int(st[:, 0].min())) * 1e3 / khz
+    total = sum(v["span_us"] for v in stats.values())
+    assert abs(total - span) <= 1e-6 * span + 1e-3, (total, span)
+    log(f"region stats: {total:.1f} us over {len(stats)} task types")
+    eng.close()
+    sched.close()
