@@ -144,7 +144,14 @@ def cpu_baseline(wl, weights, budget_s=20.0, max_steps=8):
             break
     m.close()
     per = float(np.mean(times))
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 1.0 / per, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu, "host_cpus": os.cpu_count(),
             "sample": f"{len(times)} decode steps at positions {P}..{P + len(times) - 1} of the "
                       f"{wl.name} workload (prompt KV rows filled with seeded values), "
                       f"{per * 1e3:.0f} ms/step, double-precision C++ oracle with OpenMP over output rows"}
