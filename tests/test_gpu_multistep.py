@@ -134,3 +134,38 @@ def test_region_stats_account_for_the_traced_launch():
     log(f"region stats: {total:.1f} us over {len(stats)} task types")
     eng.close()
     sched.close()
+
+
+def test_multistep_to_the_last_position_and_single_step_equivalence():
+    """Tiny decoder: greedy steps up to the last cache position in one launch
+    equal the host loop; a one-step multi-step launch equals decode_step."""
+    import torch
+    wl = synth.get("tiny")
+    w = synth.model_weights(wl, seed=1)
+    a, sa = _engine(wl, w)
+    b, sb = _engine(wl, w)
+    p0 = 4
+    for i in range(p0):
+        a.decode_step(i + 1, i)
+        b.decode_step(i + 1, i)
+    n = wl.max_ctx - p0
+    host_toks, host_logits = _host_loop(a, 9, p0, n)
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    b.decode_steps(9, p0, n, out)
+    torch.cuda.synchronize()
+    b.check()
+    assert out.cpu().numpy().tolist() == host_toks
+    assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), host_logits.view(np.uint32))
+    # rewind and take one step through each entry point
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a.decode_step(5, p0)
+    b.decode_steps(5, p0, 1, one)
+    torch.cuda.synchronize()
+    a.check()
+    b.check()
+    la, lb = a.logits.cpu().numpy(), b.logits.cpu().numpy()
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    assert int(one.cpu()[0]) == int(np.argmax(la))
+    for e, s in ((a, sa), (b, sb)):
+        e.close()
+        s.close()
