@@ -1,12 +1,15 @@
 // The persistent decode megakernel for gfx950 (CDNA4) and its engine.
 //
-// One cooperative launch per decode step; workgroup b (512 threads, 8
-// wave64s) walks queue b of the schedule: for every task it waits until its
-// counters reach epoch*P + t, runs the task's micro-kernel, and signals its
-// counters (AutoMegaKernel summary, section "Methodology", layer 0: one
-// cooperative block per multiprocessor with a local queue over a global
-// topological order, wait -> dispatch -> signal on monotonic counters, no
-// locks).  Micro-kernels (layer 1 of the same section): fused RMSNorm
+// One cooperative launch per decode step (or per n greedy steps); workgroup
+// b (512 threads, 8 wave64s) walks queue b of the schedule: for every task it
+// waits until its counters reach epoch*P + t, runs the task's micro-kernel,
+// and signals its counters (AutoMegaKernel summary, section "Methodology",
+// layer 0: one cooperative block per multiprocessor with a local queue over
+// a global topological order, wait -> dispatch -> signal on monotonic
+// counters, no locks).  With tagged activations (sync_mode 1, the default)
+// the same edges are carried by the data: every value handed between tasks
+// is a 64-bit {float, launch tag} word, a consumer's read of its inputs is
+// its wait and a producer's stores are its signal.  Micro-kernels (layer 1 of the same section): fused RMSNorm
 // prologue + GEMV for the projections, RoPE + KV append, split decode
 // attention with a log-sum-exp merge, SwiGLU, residual epilogues, LM head.
 //
@@ -230,12 +233,6 @@ __device__ __forceinline__ void argmax_block(float& best, int& bi, float* red) {
       }
     }
   __syncthreads();
-}
-
-// relaxed agent-scope load: a vector load that no cache level keeps stale
-// across the acquire done by the waiting thread
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stores of data another workgroup reads in the same launch go through at
