@@ -16,6 +16,15 @@
  * statement": single-stream batch-1 decode is bound by HBM bandwidth, with a
  * latency floor of weight bytes over bandwidth.
  *
+ * Entry points, in the order a caller uses them: amk_default_schedule_config
+ * -> amk_build_schedule -> amk_validate (the static safety gate) ->
+ * amk_pack_tensor (weights into the device layout) -> amk_engine_create ->
+ * amk_decode_step per token (or amk_decode_steps for n greedy tokens in one
+ * launch) -> amk_engine_check; amk_engine_set_trace / read_trace /
+ * region_stats time the tasks of a launch.  The dependency edges of the
+ * schedule are carried either by the counters or, by default, by tagged
+ * activation words (amk_schedule_config.sync_mode).
+ *
  * Conventions (all entry points):
  *   - plain C types only; no exception crosses the ABI; every call that can
  *     fail returns amk_status and leaves a message in amk_last_error();
