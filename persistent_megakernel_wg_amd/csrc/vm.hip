@@ -1001,6 +1001,11 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
           const uint32_t ba = bf16_bits(a), bb = bf16_bits(b);
           st_agent(row + i, (uint16_t)ba);
           st_agent(row + i + half, (uint16_t)bb);
+          // a multi-step launch reads this row from the cache in the next
+          // step: the write-through stores complete (reach the device
+          // coherence point) before the tagged copy, whose observation is
+          // the next step's licence to read the cache, is stored
+          if (P.tagged && P.tokens_out) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           if (P.tagged) {  // this launch's row for the attention tasks, as tagged bf16 values
             uint64_t* tr = P.tkv + (((int64_t)l * 2 + kvsel) * nkv + g) * hd;
             st_tag(tr + i, __uint_as_float(ba << 16), P.tag);
