@@ -86,7 +86,8 @@ typedef struct {
   int32_t attn_splits;     /* position splits per kv head (log-sum-exp merged);
                             * automatic: 3/4 of num_cus / n_kv_heads, so that
                             * a quarter of the queues run no attention split
-                            * (all of num_cus / n_kv_heads when max_ctx > 4096) */
+                            * (all of num_cus / n_kv_heads when max_ctx > 4096,
+                            * 8 when max_ctx <= 512) */
   int32_t cu_policy;       /* 0: task i of T -> queue i*num_cus/T; 1: i % num_cus */
   int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16 */
   uint32_t fuse_flags;     /* AMK_FUSE_* bits; only AMK_FUSE_DEFAULT is built */
@@ -98,9 +99,9 @@ typedef struct {
    *   the input arrived keep HBM busy while the input is staged.
    * prefetch_kb: LDS kilobytes per task into which the end of the previous
    *   task of the queue copies the task's first weight slabs (LDS DMA), so
-   *   streaming goes on through waits; 0 = 64 KB for bf16 weights (the
-   *   measured best on the 8B shape) and off for int8 / int4 weights (the
-   *   measured best there), -1 = off.
+   *   streaming goes on through waits; 0 = 64 KB for bf16 weights with
+   *   hidden >= 4096 (the measured best on the 8B shape) and off otherwise
+   *   (the measured best on the int8 / int4 and 1B workloads), -1 = off.
    * release_mode 0: all waves wait for their stores, barrier, then the
    *   release; 1: the epilogue stores and the release are issued by the
    *   polling wave alone while the others start the next task. */

@@ -57,7 +57,9 @@ amk_status amk_default_schedule_config(const amk_model_config* model, int32_t de
   // faster than the counter protocol on the 8B shape)
   c.sync_mode = 1;
   c.poll_mode = 2;  // half of the ring after the wait (measured faster on the 8B shape)
-  const int32_t splits = std::max(1, (model->max_ctx > 4096 ? 4 : 3) * device_cus / (4 * model->n_kv_heads));
+  const int32_t splits = model->max_ctx <= 512
+                             ? std::min(8, std::max(1, device_cus / model->n_kv_heads))
+                             : std::max(1, (model->max_ctx > 4096 ? 4 : 3) * device_cus / (4 * model->n_kv_heads));
   if (splits > 512 || (int64_t)splits * model->head_dim > 8192) c.sync_mode = 0;
   return resolve_config(*model, c, out);
 }

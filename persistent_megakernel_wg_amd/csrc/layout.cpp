@@ -60,8 +60,11 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   c.tiles_lm = std::min(c.tiles_lm, std::max(1, m.vocab / 2));
   // automatic split count: 3/4 of the queues run a split, all of them for
   // long contexts (more positions per step to read)
+  // (8 per kv head for caches of at most 512 positions: short splits cost
+  // more in merging than they save)
   if (c.attn_splits <= 0)
-    c.attn_splits = std::max(1, (m.max_ctx > 4096 ? 4 : 3) * c.num_cus / (4 * m.n_kv_heads));
+    c.attn_splits = m.max_ctx <= 512 ? std::min(8, std::max(1, c.num_cus / m.n_kv_heads))
+                                     : std::max(1, (m.max_ctx > 4096 ? 4 : 3) * c.num_cus / (4 * m.n_kv_heads));
   if (c.attn_splits > 256) return fail(AMK_ERR_UNSUPPORTED, "attn_splits must be at most 256");
   if (c.cu_policy != 0 && c.cu_policy != 1) return fail(AMK_ERR_UNSUPPORTED, "cu_policy must be 0 or 1");
   if (c.pipeline_depth == 0) c.pipeline_depth = 8;
@@ -84,9 +87,10 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.sync_mode < 0 || c.sync_mode > 2) return fail(AMK_ERR_UNSUPPORTED, "sync_mode must be 0, 1 or 2");
   if (c.sync_mode != 0 && (c.attn_splits > 512 || (int64_t)c.attn_splits * m.head_dim > 8192))
     return fail(AMK_ERR_UNSUPPORTED, "sync_mode 1 and 2 need attn_splits <= 512 and attn_splits * head_dim <= 8192");
-  // automatic prefetch: 64 KB for bf16 weights; off for the quantised formats,
-  // whose smaller steps gain less than the copy delays the wake
-  if (c.prefetch_kb == 0) c.prefetch_kb = m.wfmt == AMK_W_BF16 ? 64 : -1;
+  // automatic prefetch: 64 KB for bf16 weights at hidden size >= 4096; off
+  // for the quantised formats and smaller models, whose tasks gain less than
+  // the copy delays the wake (the tuner's picks on those workloads)
+  if (c.prefetch_kb == 0) c.prefetch_kb = m.wfmt == AMK_W_BF16 && m.hidden >= 4096 ? 64 : -1;
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");
   // resolved: -1 = off, else a budget in KB
