@@ -43,7 +43,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # bytes/s, MI355X published HBM3E bandwidth
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "persistent_megakernel_wg_amd", "csrc", "vm.hip")
+# sources of the decode kernel and its engine (the traffic summary is tied to them)
+KERNEL_SRCS = [os.path.join(ROOT, "persistent_megakernel_wg_amd", "csrc", f)
+               for f in ("vm.h", "vm_inst.hip", "vm.hip")]
 
 
 def log(msg):
@@ -61,8 +63,11 @@ def step_bytes(amk, model, pos):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload, nsteps_bytes):
@@ -387,7 +392,14 @@ def main():
         out["trace"] = {k: tr[k] for k in ("span_us", "wait_share", "join_latency_us")}
         out["trace"]["critical_path_us"] = {k: round(v["span_us"], 1) for k, v in tr["regions"].items()}
         log(f"trace: {json.dumps(tr)}")
-    del eng
+    # release every HIP resource before the process ends: the engine, the
+    # schedule and the device tensors are freed here, in order, not by
+    # finalizers at interpreter exit (a profiler may have detached by then)
+    eng.close()
+    sched.close()
+    del eng, dev_w, kv, logits, probe_out, big
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, weights, budget_s=args.cpu_budget)

@@ -19,20 +19,23 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "
           "-packed-fp32-ops", "-munsafe-fp-atomics"]
 HOST = ["-x", "c++", "-ffp-contract=off"]
 
-SOURCES = {  # file -> language
-    "api.cpp": "host",
-    "layout.cpp": "host",
-    "lower.cpp": "host",
-    "validate.cpp": "host",
-    "pack.cpp": "host",
-    "vm.hip": "device",
-}
+SOURCES = [  # (file, language, extra flags, object name)
+    ("api.cpp", "host", [], "api"),
+    ("layout.cpp", "host", [], "layout"),
+    ("lower.cpp", "host", [], "lower"),
+    ("validate.cpp", "host", [], "validate"),
+    ("pack.cpp", "host", [], "pack"),
+    ("vm.hip", "device", [], "vm"),
+] + [  # one object per kernel instance (pipeline depth, weight format)
+    ("vm_inst.hip", "device", [f"-DAMK_INST_DEPTH={d}", f"-DAMK_INST_WFMT={w}"], f"vm_d{d}_w{w}")
+    for d in (4, 8, 16) for w in (0, 1, 2)
+]
 
 
-def _compile(name, lang, extra):
+def _compile(name, lang, flags_extra, objname, extra):
     src = os.path.join(CSRC, name)
-    obj = os.path.join(BUILD_DIR, name + ".o")
-    flags = COMMON + (DEVICE if lang == "device" else HOST) + extra
+    obj = os.path.join(BUILD_DIR, objname + ".o")
+    flags = COMMON + (DEVICE if lang == "device" else HOST) + flags_extra + extra
     cmd = [HIPCC] + flags + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -47,8 +50,9 @@ def build(extra_flags=(), verbose=False, out=None):
     out = out or OUT
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra_flags)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=6) as ex:
-        futs = {ex.submit(_compile, n, lang, extra): n for n, lang in SOURCES.items()}
+    workers = min(16, os.cpu_count() or 4)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {ex.submit(_compile, n, lang, fl, ob, extra): ob for n, lang, fl, ob in SOURCES}
         objs = []
         for f in concurrent.futures.as_completed(futs):
             obj, msg = f.result()

@@ -44,6 +44,8 @@ def _load():
         u64, p = ctypes.c_uint64, ctypes.c_void_p
         lib.synth_normal_bf16.argtypes = [u64, u64, ctypes.c_double, u64, u64, p]
         lib.synth_normal_bf16.restype = None
+        lib.synth_normal_mean_bf16.argtypes = [u64, u64, ctypes.c_double, ctypes.c_double, u64, u64, p]
+        lib.synth_normal_mean_bf16.restype = None
         lib.synth_tokens.argtypes = [u64, u64, ctypes.c_int64, u64, p]
         lib.synth_tokens.restype = None
         lib.synth_fill_u16.argtypes = [ctypes.c_uint16, u64, p]
@@ -68,6 +70,14 @@ def normal_bf16(seed, stream, n, std=0.02, first=0, out=None):
     return out
 
 
+def normal_mean_bf16(seed, stream, n, mean, std, first=0):
+    """n samples of N(mean, std^2) as bf16 bit patterns (uint16)."""
+    out = np.empty(n, dtype=np.uint16)
+    if n:
+        _load().synth_normal_mean_bf16(seed, stream, float(mean), float(std), first, n, out.ctypes.data)
+    return out
+
+
 def fill_bf16(value_bits, n):
     out = np.empty(n, dtype=np.uint16)
     if n:
@@ -82,19 +92,40 @@ def tokens(seed, n, vocab, stream=STREAM_TOKENS):
     return out
 
 
-def model_weights(wl, seed=1, std=0.02):
+GAIN_STD = 0.25  # spread of the optional non-unit RMSNorm gains around 1
+
+
+def model_weights(wl, seed=1, std=0.02, gains="unit"):
     """Canonical bf16 tensors of a workload, keyed by canonical tensor id.
 
-    Projections and embeddings are N(0, std^2) rounded to bf16; RMSNorm
-    weights are 1.0.  Tied-embedding models have no separate lm_head.
+    Projections and embeddings are N(0, std^2) rounded to bf16.  RMSNorm
+    weights are 1.0 (gains="unit"), or with gains="random" N(1, GAIN_STD^2)
+    rounded to bf16, drawn from the norm tensor's own stream, so that a
+    gain read at the wrong index changes the result.  Tied-embedding models
+    have no separate lm_head.
     """
+    assert gains in ("unit", "random"), gains
     out = {}
     for tid, name, shape in canonical_tensors(wl):
         n = int(np.prod(shape))
-        if name.endswith("norm"):
+        if name.endswith("norm") and gains == "random":
+            out[tid] = random_gains(wl, seed)[tid]
+        elif name.endswith("norm"):
             out[tid] = fill_bf16(BF16_ONE, n).reshape(shape)
         else:
             out[tid] = normal_bf16(seed, tid, n, std).reshape(shape)
+    return out
+
+
+def random_gains(wl, seed=1):
+    """The non-unit RMSNorm gains of model_weights(gains="random"), keyed by
+    canonical tensor id: N(1, GAIN_STD^2) rounded to bf16, each from its
+    tensor's own stream.  Replacing the norms of a unit-gain weight set with
+    these gives the random-gain weight set without regenerating the rest."""
+    out = {}
+    for tid, name, shape in canonical_tensors(wl):
+        if name.endswith("norm"):
+            out[tid] = normal_mean_bf16(seed, tid, int(np.prod(shape)), 1.0, GAIN_STD).reshape(shape)
     return out
 
 

@@ -16,7 +16,9 @@
  *                u2 =  (r2>>11)    * 2^-53  in [0,1)
  *                Box-Muller (1958): rad = sqrt(-2 ln u1),
  *                element 2j = rad cos(2 pi u2), element 2j+1 = rad sin(2 pi u2)
- *   value      = bf16 round-to-nearest-even of (float)(std * z)
+ *   value      = bf16 round-to-nearest-even of (float)(mean + std * z)
+ *                (mean 0 for weights; mean 1 for the optional non-unit
+ *                RMSNorm gains)
  *   token k    = sm(key(s,t) + k) mod vocab
  */
 #include <math.h>
@@ -45,10 +47,10 @@ static inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-/* n normal samples N(0, std^2) rounded to bf16, for stream `stream`, starting
- * at element index `first` (so a tensor can be produced in pieces). */
-void synth_normal_bf16(uint64_t seed, uint64_t stream, double stdev,
-                       uint64_t first, uint64_t n, uint16_t* out) {
+/* n normal samples N(mean, std^2) rounded to bf16, for stream `stream`,
+ * starting at element index `first` (so a tensor can be produced in pieces). */
+void synth_normal_mean_bf16(uint64_t seed, uint64_t stream, double mean, double stdev,
+                            uint64_t first, uint64_t n, uint16_t* out) {
   const uint64_t key = stream_key(seed, stream);
   const double two_pi = 6.283185307179586476925286766559;
   const double inv53 = 1.0 / 9007199254740992.0; /* 2^-53 */
@@ -66,9 +68,20 @@ void synth_normal_bf16(uint64_t seed, uint64_t stream, double stdev,
     double rad = sqrt(-2.0 * log(u1));
     double ang = two_pi * u2;
     uint64_t e0 = 2 * j, e1 = 2 * j + 1;
-    if (e0 >= first && e0 < first + n) out[e0 - first] = f32_to_bf16_rne((float)(stdev * rad * cos(ang)));
-    if (e1 >= first && e1 < first + n) out[e1 - first] = f32_to_bf16_rne((float)(stdev * rad * sin(ang)));
+    double z0 = stdev * rad * cos(ang), z1 = stdev * rad * sin(ang);
+    if (mean != 0.0) { /* mean 0 keeps the signed zeros of the weight formula */
+      z0 += mean;
+      z1 += mean;
+    }
+    if (e0 >= first && e0 < first + n) out[e0 - first] = f32_to_bf16_rne((float)z0);
+    if (e1 >= first && e1 < first + n) out[e1 - first] = f32_to_bf16_rne((float)z1);
   }
+}
+
+/* N(0, std^2): the weight generator */
+void synth_normal_bf16(uint64_t seed, uint64_t stream, double stdev,
+                       uint64_t first, uint64_t n, uint16_t* out) {
+  synth_normal_mean_bf16(seed, stream, 0.0, stdev, first, n, out);
 }
 
 /* n tokens uniform in [0, vocab) for stream `stream`. */

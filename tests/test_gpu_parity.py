@@ -81,6 +81,21 @@ def test_full_size_short_prompt(name, w8b):
     log(f"{name} short: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
 
 
+def test_full_size_random_gains(w8b):
+    """8B bf16 shape with N(1, 0.25^2) bf16 RMSNorm gains at the attention,
+    MLP and final norms (the other weights as in the bench): a 3-token
+    prompt and 5 decode steps, every step compared with the oracle."""
+    wl = synth.get("8b")
+    w = dict(w8b)
+    w.update(synth.random_gains(wl, seed=1))
+    toks = synth.tokens(2, 8, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks)
+    del eng
+    _free()
+    agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
+    log(f"8b random gains: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
 @pytest.mark.parametrize("name", ["8b", "8b_int8", "8b_int4"])
 def test_full_size_long_context(name, w8b):
     """Full-size model after the workload's prompt length (1024 positions; 8192
