@@ -356,6 +356,31 @@ amk_status amk_kv_bytes(const amk_model_config* model, size_t* bytes);
 amk_status amk_engine_create(const amk_schedule* schedule, const amk_device_buffers* buffers,
                              amk_engine** out);
 
+/* Bytes of the static device scratch behind amk_engine_create_noalloc. */
+#define AMK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* amk_engine_create without any device allocation, for callers that cannot
+ * allocate device memory: code that runs under HIP graph capture, serving
+ * loops that must not call hipMalloc, harnesses that forbid allocation.
+ * Same checks, same engine and same results as amk_engine_create, but every
+ * device region the engine needs (task table, queues, RoPE table,
+ * activation scratch, counters, tagged words) is carved from one static
+ * device array of AMK_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each device for the life of the process; no hipMalloc, hipFree or other
+ * allocating routine is called (regions are zeroed and filled with
+ * hipMemset / hipMemcpy).  A schedule whose regions exceed the array ->
+ * AMK_ERR_UNSUPPORTED (the message gives both sizes) before anything is
+ * written.  The array is shared by every such engine on a device: creating
+ * one takes it over, after which an earlier engine from this call on that
+ * device fails amk_decode_step / amk_decode_steps / amk_engine_check with
+ * AMK_ERR_INVALID_ARG; using two such engines of one device concurrently,
+ * or a creation while an earlier engine's launch is still running, races.
+ * Tracing (amk_engine_set_trace) needs an allocation and is refused
+ * (AMK_ERR_UNSUPPORTED) on these engines.  amk_engine_destroy frees only
+ * the host object. */
+amk_status amk_engine_create_noalloc(const amk_schedule* schedule, const amk_device_buffers* buffers,
+                                     amk_engine** out);
+
 /* One decode step: the logits of `token` at position `pos` (fp32[vocab] into
  * buffers->logits), the KV-cache row `pos` written.  Enqueues exactly one
  * cooperative launch on hip_stream (a hipStream_t, null = default stream) and

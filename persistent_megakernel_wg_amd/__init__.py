@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNSAFE_SCHEDULE, ERR_OUT_OF_RANGE, ERR_HIP, \
     ERR_NOMEM, ERR_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # AMK_NOALLOC_SCRATCH_BYTES
 W_BF16, W_INT8_ROW, W_INT4_G128 = 0, 1, 2
 WFMT = {"bf16": W_BF16, "int8": W_INT8_ROW, "int4": W_INT4_G128}
 TASK_NOP, TASK_QKV, TASK_ATTN, TASK_MERGE, TASK_OPROJ, TASK_GATEUP, TASK_DOWN, TASK_LMHEAD = range(8)
@@ -127,6 +128,7 @@ _SIGS = {
     "amk_unpack_tensor": ([ctypes.POINTER(ModelConfig), _i32, _i32, _p, _p, _p, _p], _i32),
     "amk_kv_bytes": ([ctypes.POINTER(ModelConfig), ctypes.POINTER(ctypes.c_size_t)], _i32),
     "amk_engine_create": ([_p, ctypes.POINTER(DeviceBuffers), ctypes.POINTER(_p)], _i32),
+    "amk_engine_create_noalloc": ([_p, ctypes.POINTER(DeviceBuffers), ctypes.POINTER(_p)], _i32),
     "amk_decode_step": ([_p, _i32, _i32, _p], _i32),
     "amk_decode_steps": ([_p, _i32, _i32, _i32, _p, _p], _i32),
     "amk_engine_check": ([_p], _i32),
@@ -378,7 +380,9 @@ def unpack_tensor(model, k, canonical_id, packed, rows, cols):
 class Engine:
     """amk_engine over torch-owned device buffers (weights, KV cache, logits)."""
 
-    def __init__(self, schedule, weights, kv_cache, logits):
+    def __init__(self, schedule, weights, kv_cache, logits, noalloc=False):
+        """noalloc: bind with amk_engine_create_noalloc (the library's static
+        device scratch instead of allocations)."""
         import torch  # device memory only
         assert all(w.is_cuda for w in weights) and kv_cache.is_cuda and logits.is_cuda
         assert logits.dtype == torch.float32 and logits.is_contiguous()
@@ -387,8 +391,8 @@ class Engine:
         bufs = DeviceBuffers(ctypes.cast(self._wp, ctypes.POINTER(_p)), len(weights),
                              kv_cache.data_ptr(), ctypes.cast(logits.data_ptr(), ctypes.POINTER(_f32)))
         h = ctypes.c_void_p()
-        _check(_lib.amk_engine_create(schedule.handle, ctypes.byref(bufs), ctypes.byref(h)),
-               "amk_engine_create")
+        create = "amk_engine_create_noalloc" if noalloc else "amk_engine_create"
+        _check(getattr(_lib, create)(schedule.handle, ctypes.byref(bufs), ctypes.byref(h)), create)
         self._h = h
         self.logits = logits
         self.kv_cache = kv_cache

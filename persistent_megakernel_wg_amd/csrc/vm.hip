@@ -1,5 +1,7 @@
 // Engine of the persistent decode megakernel: device memory of a bound
 // schedule, the device task table, launches and region statistics.
+#include <mutex>
+
 #include "vm.h"
 
 namespace amk {
@@ -25,6 +27,21 @@ __global__ void __launch_bounds__(256) amk_stream_read(const uint4* __restrict__
   }
   // data-dependent store keeps the loads alive
   if (acc == 0x9E3779B9u) out[blockIdx.x] = 1.0f;
+}
+
+// Zero `n` 32-bit words (grid-stride).  Used where the engine clears device
+// state inside a caller's stream, in place of a memset node.
+__global__ void __launch_bounds__(256) amk_fill_zero(uint32_t* __restrict__ p, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// enqueue amk_fill_zero over `bytes` (a multiple of 4) at p
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const uint64_t n = bytes / 4;
+  const unsigned blocks = (unsigned)std::min<uint64_t>(1024, (n + 255) / 256 + 1);
+  hipLaunchKernelGGL(amk_fill_zero, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
 }
 
 }  // namespace amk
@@ -61,6 +78,43 @@ const void* kernel_for(int depth, int wfmt, bool multi) {
 }  // namespace
 }  // namespace amk
 
+namespace amk {
+
+// ---- the static scratch of amk_engine_create_noalloc -------------------
+// One array per device (each device that loads the library holds its own
+// copy until the process ends).  Host code never passes `scratch` itself to
+// the device: its name is a host-side stand-in; the device address is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_noalloc[device].base.
+constexpr size_t kNoAllocScratchBytes = (size_t)AMK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct NoAllocDevice {
+  uint8_t* base = nullptr;         // device address of `scratch` on this device
+  const amk_engine* owner = nullptr;  // the engine whose regions the scratch holds
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kMaxDevices];
+
+// The scratch's device address on device `dev` (the current device), looked
+// up on the first call for that device.
+amk_status noalloc_base(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(AMK_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc[dev].base) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(AMK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(err));
+    g_noalloc[dev].base = static_cast<uint8_t*>(p);
+  }
+  *out = g_noalloc[dev].base;
+  return AMK_OK;
+}
+
+}  // namespace amk
+
 struct amk_engine {
   amk_model_config model{};
   amk_schedule_config config{};
@@ -83,6 +137,10 @@ struct amk_engine {
   uint64_t* tag_arena = nullptr;
   size_t tag_arena_words = 0;
   std::vector<size_t> tag_words;
+  // amk_engine_create_noalloc: every device region of the engine is carved
+  // from this device's static scratch array (nothing allocated, nothing
+  // freed); null for engines whose regions were allocated
+  uint8_t* scratch = nullptr;
 };
 
 namespace amk {
@@ -101,17 +159,84 @@ amk_status dev_alloc(amk_engine* e, T** out, size_t count) {
   return AMK_OK;
 }
 
+// One device region of an engine: its size, where its address goes, and
+// the host bytes it starts with (null: zeros).  An engine's regions are
+// listed first and placed together, so that a schedule too large for the
+// static scratch is refused before any of it is written.
+struct Region {
+  void** dst;
+  size_t bytes;       // at least 256
+  const void* host;   // host_bytes <= bytes copied in after zeroing
+  size_t host_bytes;
+};
+
 template <typename T>
-amk_status upload(amk_engine* e, T** out, const std::vector<T>& host) {
-  amk_status st = dev_alloc(e, out, host.size());
-  if (st != AMK_OK) return st;
-  if (!host.empty()) HIP_TRY(hipMemcpy(*out, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice));
+void add_region(std::vector<Region>* r, T** dst, size_t count) {
+  r->push_back({reinterpret_cast<void**>(dst), std::max<size_t>(count * sizeof(T), 256), nullptr, 0});
+}
+
+template <typename T>
+void add_region(std::vector<Region>* r, T** dst, const std::vector<T>& host) {
+  r->push_back({reinterpret_cast<void**>(dst), std::max<size_t>(host.size() * sizeof(T), 256), host.data(),
+                host.size() * sizeof(T)});
+}
+
+constexpr size_t kRegionAlign = 256;
+inline size_t align_up(size_t v) { return (v + kRegionAlign - 1) & ~(kRegionAlign - 1); }
+
+size_t regions_bytes(const std::vector<Region>& rs) {
+  size_t off = 0;
+  for (const Region& r : rs) off = align_up(off) + r.bytes;
+  return off;
+}
+
+// Place, zero and fill the regions: from e->scratch when set, else each
+// allocated (and owned by the engine).
+amk_status place_regions(amk_engine* e, const std::vector<Region>& rs) {
+  size_t off = 0;
+  for (const Region& r : rs) {
+    void* p = nullptr;
+    if (e->scratch) {
+      off = align_up(off);
+      p = e->scratch + off;
+      off += r.bytes;
+    } else {
+      const hipError_t err = hipMalloc(&p, r.bytes);
+      if (err != hipSuccess) return fail(AMK_ERR_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(err));
+      e->owned.push_back(p);
+    }
+    HIP_TRY(hipMemset(p, 0, r.bytes));
+    if (r.host_bytes) HIP_TRY(hipMemcpy(p, r.host, r.host_bytes, hipMemcpyHostToDevice));
+    *r.dst = p;
+  }
   return AMK_OK;
 }
 
+// whether engine e may use its device regions: always for allocated
+// engines; for engines in the static scratch, only while the scratch of its
+// device still holds its regions
+bool regions_live(const amk_engine* e);
+
 void free_engine(amk_engine* e) {
   for (void* p : e->owned) (void)hipFree(p);
+  if (e->scratch) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (g_noalloc[e->device].owner == e) g_noalloc[e->device].owner = nullptr;
+  }
   delete e;
+}
+
+bool regions_live(const amk_engine* e) {
+  if (!e->scratch) return true;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  return g_noalloc[e->device].owner == e;
+}
+
+amk_status check_live(const amk_engine* e) {
+  if (!regions_live(e))
+    return fail(AMK_ERR_INVALID_ARG, "a later amk_engine_create_noalloc on this device took over the static "
+                                     "scratch that held this engine's state");
+  return AMK_OK;
 }
 
 // The kernel derives every address from (type, params) and the standard
@@ -203,18 +328,22 @@ amk_status launch_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n, in
   if (pos > e->written)
     return fail(AMK_ERR_INVALID_ARG, "pos " + std::to_string(pos) + " leaves a gap: only " +
                                          std::to_string(e->written) + " positions are written");
+  amk_status live = check_live(e);
+  if (live != AMK_OK) return live;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // (the clears below are fill kernels, not memset nodes, so that a caller
+  // may capture these launches in a HIP graph)
   // counters are monotonic across launches; restart them well before u32 wraps
   if ((uint64_t)(e->params.epoch + n + 2) * e->max_prod >= (1ull << 31)) {
-    HIP_TRY(hipMemsetAsync(e->params.ctr, 0, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
+    HIP_TRY(fill_zero(e->params.ctr, sizeof(uint32_t) * kCounterStride * e->n_counters, st));
     e->params.epoch = 0;
   }
   // a launch's tags are never reused while words of an earlier launch may
   // hold them: near the wrap the tagged words are cleared and tags start
   // again from 1
   if ((uint64_t)e->params.tag + (uint64_t)n >= 0xFFFFFFFFull) {
-    if (e->tag_arena) HIP_TRY(hipMemsetAsync(e->tag_arena, 0, e->tag_arena_words * sizeof(uint64_t), st));
-    HIP_TRY(hipMemsetAsync(e->params.targ, 0, sizeof(uint64_t) * 2 * std::max(1, e->params.n_lm), st));
+    if (e->tag_arena) HIP_TRY(fill_zero(e->tag_arena, e->tag_arena_words * sizeof(uint64_t), st));
+    HIP_TRY(fill_zero(e->params.targ, sizeof(uint64_t) * 2 * std::max(1, e->params.n_lm), st));
     e->params.tag = 1;
   }
   e->params.token = token;
@@ -234,9 +363,13 @@ amk_status launch_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n, in
 }  // namespace
 }  // namespace amk
 
-extern "C" {
+namespace amk {
+namespace {
 
-amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out) {
+// amk_engine_create (noalloc = false) and amk_engine_create_noalloc (true):
+// the same engine, with its device regions allocated or carved from the
+// device's static scratch.
+amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out, bool noalloc) {
   if (!s || !bufs || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
   *out = nullptr;
   amk_verdict v;
@@ -270,6 +403,7 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
     free_engine(e);
     return code;
   };
+  if (noalloc && (st = noalloc_base(dev, &e->scratch)) != AMK_OK) return bail(st);
 
   // ---- LDS plan (floats).  Every task uses [0, lower(task)): the head, then
   // a GEMV task's staged input and partial tables, or the attention scratch.
@@ -419,39 +553,47 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   int32_t *d_qoff = nullptr, *d_queue = nullptr;
   const uint8_t** d_wptr = nullptr;
   float2* d_rope = nullptr;
-  if ((st = upload(e, &d_tasks, dt)) != AMK_OK || (st = upload(e, &d_qoff, qoff)) != AMK_OK ||
-      (st = upload(e, &d_queue, queue)) != AMK_OK || (st = upload(e, &d_wptr, wptr)) != AMK_OK ||
-      (st = upload(e, &d_rope, rope)) != AMK_OK)
-    return bail(st);
   const int64_t L = m.n_layers, S = c.attn_splits, H = m.hidden, F = m.ffn;
   const int64_t qd = (int64_t)m.n_heads * m.head_dim;
-  if ((st = dev_alloc(e, &pr.x, (size_t)(L * 2 * H))) != AMK_OK ||
-      (st = dev_alloc(e, &pr.q, (size_t)(L * qd))) != AMK_OK ||
-      (st = dev_alloc(e, &pr.part, (size_t)(L * m.n_heads * S * (hd + 2)))) != AMK_OK ||
-      (st = dev_alloc(e, &pr.o, (size_t)(L * qd))) != AMK_OK ||
-      (st = dev_alloc(e, &pr.a, (size_t)(L * F))) != AMK_OK ||
-      (st = dev_alloc(e, &pr.ctr, (size_t)std::max(1, s->n_counters) * kCounterStride)) != AMK_OK ||
-      (st = dev_alloc(e, &pr.err, 64)) != AMK_OK)
-    return bail(st);
   pr.tagged = c.sync_mode != 0;
   pr.a_tagged = c.sync_mode == 1;
   pr.tag = 1;
   pr.n_steps = 1;
   pr.n_lm = n_lm;
   pr.tokens_out = nullptr;
-  if ((st = dev_alloc(e, &pr.targ, (size_t)std::max(1, n_lm) * 2)) != AMK_OK) return bail(st);
+  std::vector<Region> regions;
+  add_region(&regions, &d_tasks, dt);
+  add_region(&regions, &d_qoff, qoff);
+  add_region(&regions, &d_queue, queue);
+  add_region(&regions, &d_wptr, wptr);
+  add_region(&regions, &d_rope, rope);
+  add_region(&regions, &pr.x, (size_t)(L * 2 * H));
+  add_region(&regions, &pr.q, (size_t)(L * qd));
+  add_region(&regions, &pr.part, (size_t)(L * m.n_heads * S * (hd + 2)));
+  add_region(&regions, &pr.o, (size_t)(L * qd));
+  add_region(&regions, &pr.a, (size_t)(L * F));
+  add_region(&regions, &pr.ctr, (size_t)std::max(1, s->n_counters) * kCounterStride);
+  add_region(&regions, &pr.err, 64);
+  add_region(&regions, &pr.targ, (size_t)std::max(1, n_lm) * 2);
+  uint64_t* arena = nullptr;
+  e->tag_words.clear();
   if (pr.tagged) {
     const int64_t nkvd = (int64_t)m.n_kv_heads * hd;
     size_t n = 0;
-    e->tag_words.clear();
     for (int64_t w : {L * 2 * H, L * qd, L * 2 * nkvd, L * m.n_heads * S * (hd + 2), L * qd, L * F}) {
       e->tag_words.push_back((size_t)w);
       n += (size_t)w;
     }
-    uint64_t* arena = nullptr;
-    if ((st = dev_alloc(e, &arena, n)) != AMK_OK) return bail(st);
-    e->tag_arena = arena;
+    add_region(&regions, &arena, n);
     e->tag_arena_words = n;
+  }
+  if (e->scratch && regions_bytes(regions) > kNoAllocScratchBytes)
+    return bail(fail(AMK_ERR_UNSUPPORTED, "the engine needs " + std::to_string(regions_bytes(regions)) +
+                                              " bytes of device scratch; amk_engine_create_noalloc holds at most " +
+                                              std::to_string(kNoAllocScratchBytes)));
+  if ((st = place_regions(e, regions)) != AMK_OK) return bail(st);
+  if (pr.tagged) {
+    e->tag_arena = arena;
     uint64_t** dst[] = {&pr.tx, &pr.tq, &pr.tkv, &pr.tpart, &pr.to, &pr.ta};
     size_t off = 0;
     for (int k = 0; k < 6; ++k) {
@@ -482,8 +624,27 @@ amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bu
   pr.poll_late = c.poll_mode;
   pr.rel0 = c.release_mode;
   pr.spin_ticks = (uint64_t)2000000 * (uint64_t)e->wallclock_khz / 1000u;
+  if (noalloc) {
+    // the scratch now holds this engine's regions: an earlier engine made
+    // by amk_engine_create_noalloc on this device can no longer run
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    g_noalloc[dev].owner = e;
+  }
   *out = e;
   return AMK_OK;
+}
+
+}  // namespace
+}  // namespace amk
+
+extern "C" {
+
+amk_status amk_engine_create(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out) {
+  return amk::create_engine(s, bufs, out, false);
+}
+
+amk_status amk_engine_create_noalloc(const amk_schedule* s, const amk_device_buffers* bufs, amk_engine** out) {
+  return amk::create_engine(s, bufs, out, true);
 }
 
 amk_status amk_decode_step(amk_engine* e, int32_t token, int32_t pos, void* stream) {
@@ -498,6 +659,8 @@ amk_status amk_decode_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n
 
 amk_status amk_engine_check(amk_engine* e) {
   if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  amk_status live = check_live(e);
+  if (live != AMK_OK) return live;
   int32_t err = 0;
   HIP_TRY(hipMemcpy(&err, e->params.err, sizeof(err), hipMemcpyDeviceToHost));
   if (err != 0) {
@@ -519,6 +682,9 @@ amk_status amk_engine_set_kv_length(amk_engine* e, int32_t n) {
 
 amk_status amk_engine_set_trace(amk_engine* e, int32_t enable) {
   if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  if (e->scratch && enable)
+    return fail(AMK_ERR_UNSUPPORTED, "tracing allocates its stamp buffer: not available on an engine made by "
+                                     "amk_engine_create_noalloc");
   if (enable && !e->d_trace) {
     amk_status st = dev_alloc(e, &e->d_trace, (size_t)std::max(1, e->n_tasks) * 4);
     if (st != AMK_OK) return st;
