@@ -70,7 +70,7 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.pipeline_depth == 0) c.pipeline_depth = 8;
   if (c.pipeline_depth != 4 && c.pipeline_depth != 8 && c.pipeline_depth != 16)
     return fail(AMK_ERR_UNSUPPORTED, "pipeline_depth must be 4, 8 or 16");
-  if (c.poll_mode < 0 || c.poll_mode > 2) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0, 1 or 2");
+  if (c.poll_mode < 0 || c.poll_mode > 3) return fail(AMK_ERR_UNSUPPORTED, "poll_mode must be 0, 1, 2 or 3");
   if (c.release_mode != 0 && c.release_mode != 1)
     return fail(AMK_ERR_UNSUPPORTED, "release_mode must be 0 or 1");
   for (int32_t ph = 0; ph < 5; ++ph)
@@ -87,10 +87,17 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   if (c.sync_mode < 0 || c.sync_mode > 2) return fail(AMK_ERR_UNSUPPORTED, "sync_mode must be 0, 1 or 2");
   if (c.sync_mode != 0 && (c.attn_splits > 512 || (int64_t)c.attn_splits * m.head_dim > 8192))
     return fail(AMK_ERR_UNSUPPORTED, "sync_mode 1 and 2 need attn_splits <= 512 and attn_splits * head_dim <= 8192");
+  // with DMA waves, 384 threads read a merge's tagged partials in one round
+  if (c.sync_mode != 0 && c.poll_mode == 3 && (c.attn_splits > 384 || (int64_t)c.attn_splits * m.head_dim > 6144))
+    return fail(AMK_ERR_UNSUPPORTED,
+                "sync_mode 1 and 2 with poll_mode 3 need attn_splits <= 384 and attn_splits * head_dim <= 6144");
   // automatic prefetch: 64 KB for bf16 weights at hidden size >= 4096; off
   // for the quantised formats and smaller models, whose tasks gain less than
   // the copy delays the wake (the tuner's picks on those workloads)
-  if (c.prefetch_kb == 0) c.prefetch_kb = m.wfmt == AMK_W_BF16 && m.hidden >= 4096 ? 64 : -1;
+  // (with DMA waves, poll_mode 3, the copy does not delay the wake: as much
+  // as the two DMA waves and the LDS hold)
+  if (c.prefetch_kb == 0)
+    c.prefetch_kb = c.poll_mode == 3 ? 128 : (m.wfmt == AMK_W_BF16 && m.hidden >= 4096 ? 64 : -1);
   if (c.prefetch_kb != -1 && (c.prefetch_kb < 1 || c.prefetch_kb > 1024))
     return fail(AMK_ERR_INVALID_ARG, "prefetch_kb must be -1 (off) or 1..1024");
   // resolved: -1 = off, else a budget in KB

@@ -288,6 +288,20 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy);
 }
 
+// poll_mode 3 ("DMA waves"): waves kDmaWave0..7 copy the next task's first
+// weight slabs into LDS (LDS DMA) at the end of each task and issue no other
+// load before a wait; waves 0..kDmaWave0-1 read every input of a task
+// (activations, q and K/V, attention partials).  A wave's loads complete in
+// issue order, so an input read issued by a wave with a weight copy in
+// flight is only usable after that copy: keeping the two in different
+// waves lets a task take its input as soon as it is written.
+constexpr int kDmaWave0 = 6;
+__device__ __forceinline__ int input_threads(const VmParams& P) {
+  return P.poll_late == 3 ? kDmaWave0 * 64 : kThreads;
+}
+// threads that store what a counter release covers (rel0: wave 0 alone)
+__device__ __forceinline__ int epilogue_threads(const VmParams& P) { return P.rel0 ? 64 : input_threads(P); }
+
 // ------------------------------------------------------- wait / signal --
 
 // Thread 0 spins until every wait of the task holds, then performs the
@@ -396,7 +410,6 @@ __device__ __forceinline__ void trace_mark(const VmParams& P, TaskRef t, int k) 
 // meet at a barrier first.  rel0 = 1: only wave 0 issued such stores (the
 // epilogue ran on 64 threads), only it waits, and the other waves go on to
 // issue the next task's weight loads.
-__device__ __forceinline__ int epilogue_threads(const VmParams& P) { return P.rel0 ? 64 : kThreads; }
 
 __device__ __forceinline__ void vm_signal(const VmParams& P, TaskRef t) {
   const int tid = opaque_tid();
@@ -409,7 +422,9 @@ __device__ __forceinline__ void vm_signal(const VmParams& P, TaskRef t) {
     return;
   }
   if (!P.rel0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (poll_mode 3: the DMA waves stored nothing here and may be copying the
+    // next task's weights; they only meet the barrier)
+    if (tid < input_threads(P)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   if (tid < 64) {
@@ -468,6 +483,8 @@ struct GemvSplit {
 
 // attention spreads positions over waves 1..7; wave 0 polls
 constexpr int kAttnWaves = kWaves - 1;
+
+
 
 // Query heads one attention pass takes (task_attn): the group size rounded
 // up to a power of two, at most 64 lanes / (head_dim / 8 lanes per row)
@@ -561,32 +578,35 @@ struct FmtInt4 {
 // RMSNorm with bf16 gain -> optional bf16 rounding -> LDS in the chunk
 // layout of format F; int8 also gets sum x, int4 the per-chunk sums of x.
 // n is a multiple of 8.  False when a tagged read gave up.
+// Only the first `nr` threads read memory (the input, the gain); the others
+// take part in the LDS passes and barriers.
 template <class F>
 __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, const uint64_t* tsrc, int n,
                                         const uint16_t* gain, bool src_bf16, float* xs, float* red, float* xsum,
-                                        float* csum) {
+                                        float* csum, int nr) {
   const bool NORM = gain != nullptr;
   const int tid = opaque_tid(), n4 = n >> 2;
+  const bool reader = tid < nr;
   const float eps = P.eps;
   const int act_bf16 = P.act_bf16;
   float ss = 0.0f;
   // the gain of this thread's first two groups, read now so that its round
   // trip overlaps the input's
   uint2 g2[2] = {{0u, 0u}, {0u, 0u}};
-  if (NORM)
+  if (NORM && reader)
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (tid + k * kThreads < n4) g2[k] = reinterpret_cast<const uint2*>(gain)[tid + k * kThreads];
+      if (tid + k * nr < n4) g2[k] = reinterpret_cast<const uint2*>(gain)[tid + k * nr];
   if (tsrc) {  // up to 4 groups of 4 words per thread in flight at once
     TagSpin sp;
-    for (int i0 = tid; i0 < n4; i0 += kThreads * 4) {
+    for (int i0 = tid; reader && i0 < n4; i0 += nr * 4) {
       float v[16];
-      if (!ld_tagged<16>(P, tsrc, [&](int k) { return i0 + (k >> 2) * kThreads < n4; },
-                         [&](int k) { return 4 * (i0 + (k >> 2) * kThreads) + (k & 3); }, v, sp))
+      if (!ld_tagged<16>(P, tsrc, [&](int k) { return i0 + (k >> 2) * nr < n4; },
+                         [&](int k) { return 4 * (i0 + (k >> 2) * nr) + (k & 3); }, v, sp))
         break;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int i = i0 + g * kThreads;
+        const int i = i0 + g * nr;
         if (i < n4) {
           const float4 f = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
           if (NORM) ss += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
@@ -596,7 +616,7 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
     }
     if (block_any(sp.failed, red)) return false;
   } else
-  for (int i = tid; i < n4; i += kThreads) {
+  for (int i = tid; reader && i < n4; i += nr) {
     float4 v;
     if (src_bf16) {
       const uint2 b = reinterpret_cast<const uint2*>(src)[i];
@@ -615,11 +635,11 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
   if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
   else __syncthreads();
   float sx = 0.0f;
-  for (int i = tid; i < n4; i += kThreads) {
+  for (int i = tid; reader && i < n4; i += nr) {
     float4* p = reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4));
     float4 v = *p;
     if (NORM) {
-      const uint2 g = i == tid ? g2[0] : (i == tid + kThreads ? g2[1] : reinterpret_cast<const uint2*>(gain)[i]);
+      const uint2 g = i == tid ? g2[0] : (i == tid + nr ? g2[1] : reinterpret_cast<const uint2*>(gain)[i]);
       v.x = v.x * inv * bf16_lo(g.x);
       v.y = v.y * inv * bf16_hi(g.x);
       v.z = v.z * inv * bf16_lo(g.y);
@@ -710,11 +730,11 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uin
 // The GEMV proper.  The first `pf_steps` steps of every wave (fewer if the
 // wave has fewer) are already in LDS at `pf` (copied there by the end of the
 // previous task, see issue_prefetch); the register ring starts after them.
-template <class F, int DS, int RPU, typename StageFn>
+template <class F, int DS, int RPU, typename StageFn, typename AfterFn>
 __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, uint32_t row_bytes,
                                      uint32_t meta_row_bytes, int nunits, int K, const float* xs,
                                      const float* csum, float* tbl, int poll_late, int pf_steps,
-                                     const uint8_t* pf, StageFn&& stage) {
+                                     const uint8_t* pf, StageFn&& stage, AfterFn&& after_prologue) {
   const int tid = opaque_tid(), lane = tid & 63;
   const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nchunk = K / F::E;
@@ -745,8 +765,9 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
   // ring slots [0, split) are loaded before the wait, the rest after it
   // (poll_late 1: none for the polling wave; 2: half of the ring for every
   // wave, so loads issued after the input has arrived keep streaming while
-  // the input is staged)
-  const int split = poll_late == 2 ? DS / 2 : (poll_late == 1 && sw == 0 ? 0 : DS);
+  // the input is staged; 3: none: the LDS copy alone streams through the
+  // wait, and input reads queue behind no weight load)
+  const int split = poll_late == 3 ? 0 : poll_late == 2 ? DS / 2 : (poll_late == 1 && sw == 0 ? 0 : DS);
   auto prologue = [&](bool first) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -757,6 +778,7 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
   prologue(true);
   stage();
   prologue(false);
+  after_prologue();
   if (n > 0) {
     StepIter c;
     c.init(sw, nunits, J);
@@ -792,13 +814,19 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
         consume(w, m);
       }
     }
+    // Past the wave's last step the ring issues nothing: loads past the
+    // rows would return zeros without memory traffic, but each still takes
+    // its turn in the compute unit's address pipeline, where the task's
+    // epilogue stores and the next task's loads would queue behind it.
+    // (The prologue always issues its DS slots: the LDS-copy waits count
+    // them.)
     const int iters = (n - np + DS - 1) / DS;
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         consume(buf[s], mbuf[s]);
         __builtin_amdgcn_sched_barrier(0);
-        issue(buf[s], mbuf[s]);
+        if (__builtin_amdgcn_readfirstlane(it.ik) < n) issue(buf[s], mbuf[s]);
       }
     }
   }
@@ -858,20 +886,29 @@ __device__ __forceinline__ bool project(const VmParams& P, TaskRef t, float* sme
   // may be outstanding means those DMAs are done; the barrier after it shows
   // the data to every wave.
   // (poll_mode 2 issues only half of the ring before the wait.)
+  // poll_mode 3: the DMA waves issued the copies and nothing else; they
+  // wait for them after the input is staged and the ring issued, and the
+  // barrier after that shows the data to every wave.
   constexpr int kPrologueLoads = DS * RPU * (F::kMeta ? 2 : 1);
   constexpr int kHalfPrologueLoads = (DS / 2) * RPU * (F::kMeta ? 2 : 1);
-  const bool pf_wait = t.pf_have > 0 && opaque_tid() >= 64;
+  const bool dma3 = P.poll_late == 3;
+  const bool pf_wait = t.pf_have > 0 && (dma3 ? opaque_tid() >= kDmaWave0 * 64 : opaque_tid() >= 64);
   const bool half = P.poll_late == 2;
   gemv<F, DS, RPU>(ptr + (int64_t)row0 * rb, meta, rb, mb, nunits, K, xs, csum, tbl, P.poll_late,
                    t.pf_have, reinterpret_cast<const uint8_t*>(smem) + t.pf_lds, [&] {
     ok = vm_wait(P, t, flag, [&] {
-      if (pf_wait) {
+      if (pf_wait && !dma3) {
         if (half) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kHalfPrologueLoads) : "memory");
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
       }
     });
-    if (ok) ok = stage_x<F>(P, src, tsrc, K, gain, src_bf16, xs, red, xsum, csum);
+    if (ok) ok = stage_x<F>(P, src, tsrc, K, gain, src_bf16, xs, red, xsum, csum, input_threads(P));
     if (ok && P.tagged) trace_mark(P, t, 1);
+  }, [&] {
+    if (dma3 && t.pf_have > 0) {
+      if (pf_wait) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologueLoads) : "memory");
+      __syncthreads();
+    }
   });
   if (!ok) return false;
   const int J = (K / F::E + 63) >> 6;
@@ -1106,25 +1143,38 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
   const __amdgpu_buffer_rsrc_t rv = rsrc(P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd, rows_bytes);
   const uint32_t lane_off = (uint32_t)li * 16u, row_b = (uint32_t)hd * 2u;
   // waves 1..7 take the positions; wave 0 polls and keeps no loads in flight
+  // (poll_mode 3: waves 0..kDmaWave0-1 take them, the DMA waves none)
   const int wsc = __builtin_amdgcn_readfirstlane(wave);
+  const int aw0 = P.poll_late == 3 ? 0 : 1;
+  const int naw = P.poll_late == 3 ? kDmaWave0 : kAttnWaves;
+  const bool aw = wsc >= aw0 && wsc < aw0 + naw;  // this wave takes positions
+  const int wi = wsc - aw0;
   auto posof = [&](int blk, int c) {
-    return p0 + ((blk * MAXC + c) * kAttnWaves + (wsc - 1)) * PW + pw;
+    return p0 + ((blk * MAXC + c) * naw + wi) * PW + pw;
   };
   auto koff = [&](int j, bool ok) { return ok ? (uint32_t)j * row_b + lane_off : kOob; };
   // two register buffers of blocks: blocks 0 and 1 are loaded before the
   // wait (positions before pos only: rows of earlier launches); later blocks
   // are loaded into the buffer just consumed, two blocks ahead
   u32x4 ka[MAXC], va[MAXC], kb[MAXC], vb[MAXC];
+  // a chunk whose first position (lane group 0) is past the split holds no
+  // position of this wave: zeros, without a load (an out-of-range load
+  // would still take a turn in the address pipeline)
   auto load_blk = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk, bool before_wait) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int j = posof(blk, c);
-      const uint32_t o = koff(j, j < p1 && (!before_wait || j < pos));
-      k[c] = bload(rk, o);
-      v[c] = bload(rv, o);
+      if (__builtin_amdgcn_readfirstlane(j - pw) < p1) {
+        const uint32_t o = koff(j, j < p1 && (!before_wait || j < pos));
+        k[c] = bload(rk, o);
+        v[c] = bload(rv, o);
+      } else {
+        k[c] = u32x4{0u, 0u, 0u, 0u};
+        v[c] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  if (wsc != 0) {
+  if (aw) {
     load_blk(ka, va, 0, true);
     load_blk(kb, vb, 1, true);
   }
@@ -1141,8 +1191,8 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
   u32x4 kp = {0u, 0u, 0u, 0u}, vp = {0u, 0u, 0u, 0u};
   if (tagged) {
     const int d = pos - p0 - pw;
-    if (wsc != 0 && pos < p1 && d >= 0 && d % PW == 0 && (d / PW) % kAttnWaves == wsc - 1) {
-      const int bc = d / PW / kAttnWaves;
+    if (aw && pos < p1 && d >= 0 && d % PW == 0 && (d / PW) % naw == wi) {
+      const int bc = d / PW / naw;
       pblk = bc / MAXC;
       pc = bc % MAXC;
     }
@@ -1152,7 +1202,7 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
     const int64_t kd = (P.tkv - P.tq) + (((int64_t)l * 2 + 0) * P.nkv + g) * hd + li * 8 - qoff;
     const int64_t vd = (P.tkv - P.tq) + (((int64_t)l * 2 + 1) * P.nkv + g) * hd + li * 8 - qoff;
     float v[24];
-    if (ld_tagged<24>(P, P.tq + qoff, [&](int k) { return k < 8 || pblk >= 0; },
+    if (ld_tagged<24>(P, P.tq + qoff, [&](int k) { return aw && (k < 8 || pblk >= 0); },
                       [&](int k) { return k < 8 ? (int64_t)k : (k < 16 ? kd + (k - 8) : vd + (k - 16)); }, v, sp)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) q[e] = v[e] * scale;
@@ -1162,9 +1212,12 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
     }
     if (block_any(sp.failed, smem)) return false;
   } else {
-    const float* qp = P.q + qoff;
-    const float4 a = *reinterpret_cast<const float4*>(qp);
-    const float4 b = *reinterpret_cast<const float4*>(qp + 4);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (aw) {
+      const float* qp = P.q + qoff;
+      a = *reinterpret_cast<const float4*>(qp);
+      b = *reinterpret_cast<const float4*>(qp + 4);
+    }
     q[0] = a.x * scale; q[1] = a.y * scale; q[2] = a.z * scale; q[3] = a.w * scale;
     q[4] = b.x * scale; q[5] = b.y * scale; q[6] = b.z * scale; q[7] = b.w * scale;
   }
@@ -1173,8 +1226,8 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   const int len = p1 - p0;
-  const int per_blk = MAXC * kAttnWaves * PW;
-  const int nblk = wsc == 0 ? 0 : (len + per_blk - 1) / per_blk;
+  const int per_blk = MAXC * naw * PW;
+  const int nblk = aw ? (len + per_blk - 1) / per_blk : 0;
   // the row at pos (written by this launch) in a block loaded before the wait
   auto patch_pos = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk) {
 #pragma unroll
@@ -1359,20 +1412,24 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
   float* wts = wsum + S * hd;      // [S]
   float2 ml = make_float2(-INFINITY, 0.0f);
   const int items = S * hq;
+  // the first nr threads read (poll_mode 3: not the DMA waves, which may be
+  // copying the next task's weights)
+  const int nr = input_threads(P);
+  const bool reader = tid < nr;
   float4 ch[4];
   if (P.tagged) {
     // the partials are tagged words: one round of reads (this thread's four
     // chunks and its split's (max, sum)), then re-reads until tagged.  The
-    // engine admits the tagged mode only where S <= kThreads and
-    // S * hd / 4 <= 4 * kThreads, so these cover every item.
+    // engine admits the tagged mode only where S <= nr and
+    // S * hd / 4 <= 4 * nr, so these cover every item.
     const uint64_t* tp = P.tpart + pbase;
     TagSpin spn;
     float v[18];
     ld_tagged<18>(
-        P, tp, [&](int k) { return k < 16 ? tid + (k >> 2) * kThreads < items : tid < S; },
+        P, tp, [&](int k) { return reader && (k < 16 ? tid + (k >> 2) * nr < items : tid < S); },
         [&](int k) {
           if (k >= 16) return (int64_t)tid * (hd + 2) + hd + (k - 16);
-          const int it = tid + (k >> 2) * kThreads, sp = it / hq, qd = it - sp * hq;
+          const int it = tid + (k >> 2) * nr, sp = it / hq, qd = it - sp * hq;
           return (int64_t)sp * (hd + 2) + qd * 4 + (k & 3);
         },
         v, spn);
@@ -1380,12 +1437,12 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
     trace_mark(P, t, 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) ch[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    if (tid < S) ml = make_float2(v[16], v[17]);
-  } else {
+    if (reader && tid < S) ml = make_float2(v[16], v[17]);
+  } else if (reader) {
     if (tid < S) ml = *reinterpret_cast<const float2*>(part + (int64_t)tid * (hd + 2) + hd);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int it = tid + k * kThreads;
+      const int it = tid + k * nr;
       if (it < items) {
         const int sp = it / hq, qd = it - sp * hq;
         ch[k] = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
@@ -1393,7 +1450,7 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
     }
   }
   float m = ml.x;
-  for (int sp = tid + kThreads; sp < S; sp += kThreads) m = fmaxf(m, part[(int64_t)sp * (hd + 2) + hd]);
+  for (int sp = tid + nr; reader && sp < S; sp += nr) m = fmaxf(m, part[(int64_t)sp * (hd + 2) + hd]);
   m = wave_max(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
@@ -1402,12 +1459,12 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
   for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, red[w]);
   __syncthreads();
   float lsum = 0.0f;
-  if (tid < S) {
+  if (reader && tid < S) {
     const float wgt = ml.x == -INFINITY ? 0.0f : __expf(ml.x - Mx);
     wts[tid] = wgt;
     lsum = wgt * ml.y;
   }
-  for (int sp = tid + kThreads; sp < S; sp += kThreads) {
+  for (int sp = tid + nr; reader && sp < S; sp += nr) {
     const float ms = part[(int64_t)sp * (hd + 2) + hd];
     const float wgt = ms == -INFINITY ? 0.0f : __expf(ms - Mx);
     wts[sp] = wgt;
@@ -1416,15 +1473,15 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
   const float Ltot = block_sum(lsum, red);  // its barriers also publish wts
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int it = tid + k * kThreads;
-    if (it < items) {
+    const int it = tid + k * nr;
+    if (reader && it < items) {
       const int sp = it / hq, qd = it - sp * hq;
       const float wgt = wts[sp];
       *reinterpret_cast<float4*>(wsum + sp * hd + qd * 4) =
           make_float4(wgt * ch[k].x, wgt * ch[k].y, wgt * ch[k].z, wgt * ch[k].w);
     }
   }
-  for (int it = tid + 4 * kThreads; it < items; it += kThreads) {
+  for (int it = tid + 4 * nr; reader && it < items; it += nr) {
     const int sp = it / hq, qd = it - sp * hq;
     const float4 c = *reinterpret_cast<const float4*>(part + (int64_t)sp * (hd + 2) + qd * 4);
     const float wgt = wts[sp];
@@ -1432,14 +1489,23 @@ __device__ __forceinline__ bool task_merge(const VmParams& P, TaskRef t, float* 
   }
   __syncthreads();
   const float inv = 1.0f / Ltot;
+  // the sum over splits: Q = kThreads / hd threads per output element each
+  // add every Q-th split (Q dependent LDS reads in flight instead of one
+  // chain of S), then the Q partial sums are added in a fixed order
+  const int Q = kThreads / hd, e0 = tid % hd, q0 = tid / hd;
+  float v = 0.0f;
+  for (int sp = q0; sp < S; sp += Q) v += wsum[sp * hd + e0];
+  __syncthreads();
+  wsum[q0 * hd + e0] = v;  // rows 0..Q-1 (inside the attention scratch also when S < Q)
+  __syncthreads();
   const int EW = epilogue_threads(P);
   if (tid < EW)
     for (int e = tid; e < hd; e += EW) {
-      float v = 0.0f;
-      for (int sp = 0; sp < S; ++sp) v += wsum[sp * hd + e];
+      float tot = 0.0f;
+      for (int k = 0; k < Q; ++k) tot += wsum[k * hd + e];
       const int64_t o = (int64_t)l * P.nq * hd + (int64_t)h * hd + e;
-      if (P.tagged) st_tag(P.to + o, v * inv, P.tag);
-      else st_agent(P.o + o, v * inv);
+      if (P.tagged) st_tag(P.to + o, tot * inv, P.tag);
+      else st_agent(P.o + o, tot * inv);
     }
   vm_signal(P, t);
   return true;
@@ -1492,14 +1558,20 @@ __device__ __forceinline__ void issue_prefetch_rpu(const VmParams& P, const PfNe
   const int jl = (nchunk - lane + 63) >> 6;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)t.lds);
   constexpr uint32_t kStep = pf_row_step<F>();
-  for (int pass = 0; pass < 2; ++pass) {
-    const int v = pass == 0 ? sw : 0;  // own slabs, then a share of wave 0's
+  // poll_mode 3: DMA wave kDmaWave0 + i copies all slabs of waves
+  // i*per .. i*per + per - 1; otherwise waves 1..7 copy their own slabs
+  // and a share of wave 0's (which polls)
+  const bool dma3 = P.poll_late == 3;
+  constexpr int per = kWaves / (kWaves - kDmaWave0);
+  const int npass = dma3 ? per : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int v = dma3 ? (sw - kDmaWave0) * per + pass : (pass == 0 ? sw : 0);
     StepIter it;
     it.init(v, nunits, J);
     const int np = min(steps, it.n);
     const uint32_t area = lds0 + (uint32_t)v * (uint32_t)steps * RPU * kStep;
     for (int k = 0; k < np; ++k) {
-      if (v == sw || k % (kWaves - 1) == sw - 1) {
+      if (dma3 || v == sw || k % (kWaves - 1) == sw - 1) {
         const bool valid = it.ij < jl;
         const uint32_t off = (uint32_t)it.iu * RPU * rb + (uint32_t)(it.ij * 64 + lane) * 16u;
         const uint32_t moff = (uint32_t)it.iu * RPU * mb + (uint32_t)(it.ij * 16 + (lane >> 2)) * 4u;
@@ -1519,7 +1591,7 @@ template <int WFMT>
 __device__ __forceinline__ void issue_prefetch(const VmParams& P, const PfNext& t, float* smem) {
   if (t.steps <= 0) return;
   const int sw = __builtin_amdgcn_readfirstlane(opaque_tid() >> 6);
-  if (sw == 0) return;
+  if (P.poll_late == 3 ? sw < kDmaWave0 : sw == 0) return;
   if (t.rpu == 2) issue_prefetch_rpu<WFMT, 2>(P, t, smem, sw);
   else issue_prefetch_rpu<WFMT, 1>(P, t, smem, sw);
 }

@@ -504,9 +504,14 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
         const Task& b = s->tasks[q[k]];
         const GemvShape g = gemv_shape(m, b);
         if (!g.rpu) continue;
+        // the issuer steps back over MERGE tasks (and, with DMA waves,
+        // over ATTN tasks too: their input reads and the copy are in
+        // different waves, so the O projection streams during attention)
+        const bool dma3 = c.poll_mode == 3;
+        auto skip = [&](int32_t ty) { return ty == AMK_TASK_MERGE || (dma3 && ty == AMK_TASK_ATTN); };
         size_t j = k - 1;
         int64_t used_f = lower(b);
-        while (j > 0 && s->tasks[q[j]].type == AMK_TASK_MERGE) used_f = std::max(used_f, lower(s->tasks[q[j--]]));
+        while (j > 0 && skip(s->tasks[q[j]].type)) used_f = std::max(used_f, lower(s->tasks[q[j--]]));
         used_f = std::max(used_f, lower(s->tasks[q[j]]));
         const int32_t prev_ty = s->tasks[q[k - 1]].type;
         const int32_t kb = prev_ty == AMK_TASK_ATTN || prev_ty == AMK_TASK_MERGE ? c.prefetch_attn_kb : c.prefetch_kb;
@@ -515,7 +520,11 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
         const int64_t step = g.rpu * per_row;
         const int64_t used = 4 * used_f;
         const int64_t avail = std::min<int64_t>(lds_total - used - 64, (int64_t)kb * 1024);
-        const int64_t dma_cap = 49 / (g.rpu * (m.wfmt == AMK_W_INT4_G128 ? 2 : 1));
+        // DMA loads outstanding per issuing wave: about 56 when waves 1..7
+        // each copy their own steps and a seventh of wave 0's; at most 60
+        // when each of the two DMA waves copies the steps of four waves
+        const int64_t loads_per_step = g.rpu * (m.wfmt == AMK_W_INT4_G128 ? 2 : 1);
+        const int64_t dma_cap = dma3 ? 60 / (4 * loads_per_step) : 49 / loads_per_step;
         const int64_t steps = std::min<int64_t>(avail / (kWaves * step), dma_cap);
         if (steps < 1) continue;
         const int64_t off = lds_total - kWaves * steps * step;

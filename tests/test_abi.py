@@ -138,7 +138,7 @@ def test_invalid_schedule_configs():
     for field, value, code in [("pipeline_depth", 5, amk.ERR_UNSUPPORTED), ("attn_splits", 300, amk.ERR_UNSUPPORTED),
                                ("cu_policy", 2, amk.ERR_UNSUPPORTED), ("fuse_flags", 0x3, amk.ERR_UNSUPPORTED),
                                ("wg_threads", 256, amk.ERR_UNSUPPORTED), ("num_cus", 0, amk.ERR_INVALID_ARG),
-                               ("poll_mode", 3, amk.ERR_UNSUPPORTED), ("release_mode", 3, amk.ERR_UNSUPPORTED)]:
+                               ("poll_mode", 4, amk.ERR_UNSUPPORTED), ("release_mode", 3, amk.ERR_UNSUPPORTED)]:
         c = amk.default_schedule_config(m, 8)
         setattr(c, field, value)
         expect_status(code, amk.Schedule.build, m, c)
@@ -243,6 +243,17 @@ def test_sync_mode_limits():
         s = amk.Schedule.build(m, c)
         assert s.validate() == (0, -1, -1, -1)
         s.close()
+    # with DMA waves (poll_mode 3), 384 threads read a merge's partials:
+    # tagged modes need attn_splits * head_dim <= 6144 (48 splits at 128)
+    for mode, splits, ok in ((1, 48, True), (1, 49, False), (2, 49, False), (0, 49, True)):
+        c = amk.default_schedule_config(m, 256)
+        c.sync_mode, c.attn_splits, c.poll_mode = mode, splits, 3
+        if ok:
+            s = amk.Schedule.build(m, c)
+            assert s.validate() == (0, -1, -1, -1)
+            s.close()
+        else:
+            expect_status(amk.ERR_UNSUPPORTED, amk.Schedule.build, m, c)
     # the default falls back to counters where the split count is too large
     c = amk.default_schedule_config(amk.ModelConfig.from_workload(synth.get("8b").with_(n_kv_heads=1, n_heads=16)), 256)
     assert c.sync_mode == 0

@@ -120,7 +120,12 @@ def test_full_size_long_context(name, w8b):
                                    {"release_mode": 1}, {"pipeline_depth": 4}, {"pipeline_depth": 16},
                                    {"cu_policy": 1}, {"attn_splits": 3}, {"merge_place": 1},
                                    {"sync_mode": 1}, {"sync_mode": 2}, {"sync_mode": 1, "attn_splits": 3},
-                                   {"sync_mode": 1, "prefetch_kb": -1, "prefetch_attn_kb": -1}],
+                                   {"sync_mode": 1, "prefetch_kb": -1, "prefetch_attn_kb": -1},
+                                   {"poll_mode": 3}, {"poll_mode": 3, "sync_mode": 0},
+                                   {"poll_mode": 3, "sync_mode": 2}, {"poll_mode": 3, "sync_mode": 0, "release_mode": 1},
+                                   {"poll_mode": 3, "release_mode": 1}, {"poll_mode": 3, "prefetch_kb": 4},
+                                   {"poll_mode": 3, "attn_splits": 3}, {"poll_mode": 3, "pipeline_depth": 16},
+                                   {"poll_mode": 3, "prefetch_kb": -1, "prefetch_attn_kb": -1}],
                          ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_schedule_knobs_keep_parity(sched):
     """Every ScheduleConfig knob the kernel reads, on the tiny decoder's full
