@@ -216,6 +216,8 @@ def main():
     ap.add_argument("--trace", default="", help="after timing, trace 2 steps and write the analysis here")
     ap.add_argument("--prompt-kv", choices=("decode", "synthetic"), default="decode")
     ap.add_argument("--probe", choices=("", "copy"), default="")
+    ap.add_argument("--no-counter-protocol", action="store_true",
+                    help="skip timing the same positions with the counter protocol (sync_mode 0)")
     ap.add_argument("--multistep", action="store_true",
                     help="also time the same positions as one greedy multi-step launch")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -342,12 +344,14 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
-    # the fraction of a plain streaming read's rate on the same device: a
-    # grid-stride read of the largest weight tensor (amk_stream_read_probe)
+    # the fraction of the device's streaming-read ceiling: the largest weight
+    # tensor read in the pattern that reaches the highest rate here
+    # (amk_stream_read_probe: contiguous share per workgroup, 16
+    # non-temporal 16-byte loads per lane in flight), best of three grids
     big = max(dev_w, key=lambda x: x.numel() * x.element_size())
     probe_out = torch.zeros(65536, device=dev)
     rates = []
-    for blocks in (2048, 8192):
+    for blocks in (256, 512, 1024):
         amk.stream_read_probe(big, probe_out, blocks)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -358,6 +362,36 @@ def main():
         rates.append(big.numel() * big.element_size() * 5 / (e0.elapsed_time(e1) * 1e-3))
     out["stream_read"] = {"GBps": max(rates) / 1e9, "bytes": int(big.numel() * big.element_size()),
                           "kernel_frac": achieved / max(rates)}
+    if not args.no_counter_protocol and cfg.sync_mode != 0:
+        # the same positions with the pages' counter protocol (sync_mode 0):
+        # same DAG, every edge a monotonic counter (wait -> dispatch ->
+        # signal) instead of a tagged activation word
+        c0 = amk.ScheduleConfig.from_buffer_copy(cfg)
+        c0.sync_mode = 0
+        s0 = amk.Schedule.build(model, c0)
+        assert s0.validate()[0] == 0
+        kv0, lg0 = amk.alloc_state(model, device=dev)
+        kv0.copy_(kv)
+        e_c = amk.Engine(s0, dev_w, kv0, lg0)
+        e_c.set_kv_length(P)
+        for i in range(args.warmup):
+            e_c.decode_step(int(toks[P + i]), P + i, stream)
+        torch.cuda.synchronize()
+        e_c.check()
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for i in range(steps):
+            e_c.decode_step(int(dec[i]), P + i, stream)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        e_c.check()
+        ms = m0.elapsed_time(m1) / steps
+        out["counter_protocol"] = {"sync_mode": 0, "ms_per_step": ms, "tokens_per_s": 1e3 / ms,
+                                   "floor_fraction": float(tmin.mean() / (ms * 1e-3))}
+        log(f"counter protocol (sync_mode 0): {ms:.4f} ms/step")
+        e_c.close()
+        s0.close()
+        del e_c, kv0, lg0
     if args.multistep:
         # the same positions decoded greedily in ONE launch (amk_decode_steps):
         # the token of every step is fed back on the device

@@ -299,6 +299,17 @@ amk_status amk_build_schedule(const amk_model_config* model, const amk_schedule_
  * naming the first failure.  Host only, never touches a GPU. */
 amk_status amk_validate(const amk_schedule* schedule, amk_verdict* out);
 
+/* Whether a schedule may run greedy multi-step launches (amk_decode_steps).
+ * Step s + 1 starts on a queue once that queue finished step s and every
+ * LM-head task of step s stored its argmax partial; so every task must
+ * happen-before some LM-head task (through queue order and full-join waits,
+ * the gate's happens-before), else a step s + 1 store could overtake a read
+ * of step s that is still running.  AMK_OK if that holds (*task = -1);
+ * AMK_ERR_UNSUPPORTED with *task = the smallest task that is no such
+ * ancestor (or -2: no LM-head task); AMK_ERR_UNSAFE_SCHEDULE if the gate
+ * (amk_validate) rejects the schedule.  Host only. */
+amk_status amk_multistep_check(const amk_schedule* schedule, int32_t* task);
+
 /* Flat view of a schedule; the arrays stay valid until amk_schedule_free. */
 amk_status amk_schedule_view(const amk_schedule* schedule, amk_schedule_desc* out);
 
@@ -403,6 +414,8 @@ amk_status amk_decode_step(amk_engine* engine, int32_t token, int32_t pos, void*
  * otherwise as amk_decode_step. */
 amk_status amk_decode_steps(amk_engine* engine, int32_t token, int32_t pos, int32_t n_steps,
                             int32_t* tokens_out, void* hip_stream);
+/* (AMK_ERR_UNSUPPORTED, before anything is enqueued, when the engine's
+ * schedule fails amk_multistep_check.) */
 
 /* Declare that KV-cache rows 0..n_positions-1 already hold valid state the
  * caller wrote (a restored cache, or a prefix filled outside the library), so
@@ -455,10 +468,14 @@ amk_status amk_engine_steps(const amk_engine* engine, int64_t* out);
 
 amk_status amk_engine_destroy(amk_engine* engine);
 
-/* Measurement utility, not part of the decode path: one plain streaming-read
- * launch over `bytes` (a multiple of 16) of device memory `src`, `blocks`
- * workgroups of 256 threads, one float per block written to device `out`
- * (blocks floats).  Enqueued on hip_stream; time it with events. */
+/* Measurement utility, not part of the decode path: one streaming read of
+ * `bytes` (a multiple of 16, below 2 GiB) of device memory `src` in the
+ * pattern that reaches the highest read rate this device sustains (each of
+ * `blocks` workgroups of 512 threads reads one contiguous share in 1 KB
+ * slabs, 16 non-temporal 16-byte loads per lane in flight); one float per
+ * workgroup may be written to device `out` (blocks floats).  Enqueued on
+ * hip_stream; time it with events.  AMK_ERR_INVALID_ARG for null pointers,
+ * blocks < 1 or a bad size. */
 amk_status amk_stream_read_probe(const void* src, size_t bytes, float* out, int32_t blocks,
                                  void* hip_stream);
 

@@ -119,6 +119,7 @@ _SIGS = {
     "amk_default_schedule_config": ([ctypes.POINTER(ModelConfig), _i32, ctypes.POINTER(ScheduleConfig)], _i32),
     "amk_build_schedule": ([ctypes.POINTER(ModelConfig), ctypes.POINTER(ScheduleConfig), ctypes.POINTER(_p)], _i32),
     "amk_validate": ([_p, ctypes.POINTER(Verdict)], _i32),
+    "amk_multistep_check": ([_p, ctypes.POINTER(_i32)], _i32),
     "amk_schedule_view": ([_p, ctypes.POINTER(ScheduleDesc)], _i32),
     "amk_schedule_from_desc": ([ctypes.POINTER(ScheduleDesc), ctypes.POINTER(_p)], _i32),
     "amk_schedule_free": ([_p], None),
@@ -198,6 +199,16 @@ class Schedule:
         if st not in (OK, ERR_UNSAFE_SCHEDULE):
             _check(st, "amk_validate")
         return v.astuple()
+
+    def multistep_check(self):
+        """(status, task) of amk_multistep_check: OK and -1 when greedy
+        multi-step launches are safe, else the first task that happens-before
+        no LM-head task (-2: there is none)."""
+        t = _i32()
+        st = _lib.amk_multistep_check(self._h, ctypes.byref(t))
+        if st not in (OK, ERR_UNSUPPORTED):
+            _check(st, "amk_multistep_check")
+        return st, t.value
 
     def view(self):
         """Plain-Python copy of the flat schedule description."""

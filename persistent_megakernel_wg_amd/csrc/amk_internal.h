@@ -116,6 +116,14 @@ void sort_accesses(std::vector<Access>* a);
 
 amk_verdict validate(const amk_schedule& s);
 
+// Greedy multi-step launches (amk_decode_steps) start step s + 1 on each
+// queue once every LM-head task of step s has stored its argmax partial, so
+// they are safe only if every task happens-before some LM-head task (then no
+// step s + 1 store can overtake a step s read).  Returns the smallest task
+// that is not such an ancestor, -1 if there is none, -2 if the schedule has
+// no LM-head task.  Expects a schedule that passed validate().
+int32_t multistep_unsafe_task(const amk_schedule& s);
+
 // ----------------------------------------------------- device records --
 constexpr int kMaxWaits = 4;
 constexpr int kMaxSigs = 4;

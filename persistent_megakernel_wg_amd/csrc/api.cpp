@@ -106,6 +106,24 @@ amk_status amk_validate(const amk_schedule* s, amk_verdict* out) {
   return AMK_OK;
 }
 
+amk_status amk_multistep_check(const amk_schedule* s, int32_t* task) {
+  if (!s || !task) return fail(AMK_ERR_INVALID_ARG, "null argument");
+  amk_verdict v;
+  const amk_status st = amk_validate(s, &v);
+  if (st != AMK_OK) return st;
+  try {
+    *task = multistep_unsafe_task(*s);
+  } catch (const std::bad_alloc&) {
+    return fail(AMK_ERR_NOMEM, "out of host memory while checking");
+  }
+  if (*task == -2) return fail(AMK_ERR_UNSUPPORTED, "multi-step decoding needs LM-head tasks");
+  if (*task >= 0)
+    return fail(AMK_ERR_UNSUPPORTED, "task " + std::to_string(*task) +
+                                         " happens-before no LM-head task: a multi-step launch could start the "
+                                         "next step while it still runs");
+  return AMK_OK;
+}
+
 amk_status amk_schedule_view(const amk_schedule* s, amk_schedule_desc* out) {
   if (!s || !out) return fail(AMK_ERR_INVALID_ARG, "null argument");
   const int32_t nt = (int32_t)s->tasks.size();

@@ -307,4 +307,46 @@ amk_verdict validate(const amk_schedule& s) {
   return verdict(AMK_V_OK);
 }
 
+// Multi-step safety: the smallest task that is not a happens-before
+// ancestor (queue edges and full-join wait edges, transitively) of any
+// LM-head task, -1 when every task is one, -2 without LM-head tasks.
+int32_t multistep_unsafe_task(const amk_schedule& s) {
+  const int32_t nt = (int32_t)s.tasks.size(), nc = s.n_counters;
+  const std::vector<uint32_t> P = counter_producers(s);
+  // reverse edges of the happens-before graph: waiter -> counter -> producer,
+  // queue successor -> predecessor
+  std::vector<std::pair<int32_t, int32_t>> rev;
+  for (int32_t i = 0; i < nt; ++i) {
+    for (int32_t c : s.tasks[i].sigs)
+      if (c >= 0 && c < nc) rev.push_back({nt + c, i});
+    for (const Wait& w : s.tasks[i].waits)
+      if (w.ctr >= 0 && w.ctr < nc && w.thr == P[w.ctr]) rev.push_back({i, nt + w.ctr});
+  }
+  for (const auto& q : s.queues)
+    for (size_t i = 1; i < q.size(); ++i)
+      if (q[i] >= 0 && q[i] < nt && q[i - 1] >= 0 && q[i - 1] < nt) rev.push_back({q[i], q[i - 1]});
+  Csr g;
+  g.build(nt + nc, rev);
+  std::vector<char> anc(nt + nc, 0);
+  std::vector<int32_t> work;
+  for (int32_t i = 0; i < nt; ++i)
+    if (s.tasks[i].type == AMK_TASK_LMHEAD) {
+      anc[i] = 1;
+      work.push_back(i);
+    }
+  if (work.empty()) return -2;
+  while (!work.empty()) {
+    const int32_t v = work.back();
+    work.pop_back();
+    for (int32_t e = g.off[v]; e < g.off[v + 1]; ++e)
+      if (!anc[g.adj[e]]) {
+        anc[g.adj[e]] = 1;
+        work.push_back(g.adj[e]);
+      }
+  }
+  for (int32_t i = 0; i < nt; ++i)
+    if (!anc[i]) return i;
+  return -1;
+}
+
 }  // namespace amk

@@ -6,26 +6,36 @@
 
 namespace amk {
 
-// Plain streaming read of `bytes` (multiple of 16): grid-stride 16-byte
-// loads, 4 in flight per thread, one partial sum per block so the loads are
-// not dead.  Measures the read bandwidth the memory system sustains.
-__global__ void __launch_bounds__(256) amk_stream_read(const uint4* __restrict__ src, uint64_t n16,
+// Streaming read of `bytes` (multiple of 16) at the rate the memory system
+// sustains for this access pattern: workgroup b of G (512 threads) reads one
+// contiguous 1/G of the buffer in 1 KB slabs (64 lanes x 16 bytes), its 8
+// waves taking every 8th slab, 16 non-temporal loads per lane in flight.
+// Loads past `bytes` return zero (buffer range check).  One word per
+// workgroup is stored only if the data hash hits a constant, which keeps the
+// loads live.
+constexpr int kStreamDepth = 16;
+__global__ void __launch_bounds__(512) amk_stream_read(const uint8_t* __restrict__ src, uint32_t bytes,
                                                         float* __restrict__ out) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t nslab = ((uint64_t)bytes + 1023) / 1024;
+  const uint64_t s0 = nslab * blockIdx.x / gridDim.x, s1 = nslab * (blockIdx.x + 1) / gridDim.x;
+  const __amdgpu_buffer_rsrc_t r = rsrc(src, bytes);
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i];
-    const uint4 b = src[i + stride];
-    const uint4 c = src[i + 2 * stride];
-    const uint4 d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  u32x4 buf[kStreamDepth];
+  auto off = [&](uint64_t k) {  // k-th slab of this wave
+    const uint64_t sl = s0 + (uint64_t)w + 8 * k;
+    return sl < s1 ? (uint32_t)(sl * 1024 + (uint64_t)lane * 16) : kOob;
+  };
+  const uint64_t n = (s1 - s0 + 7 - (uint64_t)w) / 8;  // slabs of this wave
+#pragma unroll
+  for (int k = 0; k < kStreamDepth; ++k) buf[k] = bload(r, off(k));
+  for (uint64_t i = 0; i < n; i += kStreamDepth) {
+#pragma unroll
+    for (int k = 0; k < kStreamDepth; ++k) {
+      acc ^= buf[k].x ^ buf[k].y ^ buf[k].z ^ buf[k].w;
+      if (i + kStreamDepth + k < n) buf[k] = bload(r, off(i + kStreamDepth + k));
+    }
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
-  // data-dependent store keeps the loads alive
   if (acc == 0x9E3779B9u) out[blockIdx.x] = 1.0f;
 }
 
@@ -137,6 +147,8 @@ struct amk_engine {
   uint64_t* tag_arena = nullptr;
   size_t tag_arena_words = 0;
   std::vector<size_t> tag_words;
+  // the schedule passes amk_multistep_check (amk_decode_steps allowed)
+  bool multistep_ok = false;
   // amk_engine_create_noalloc: every device region of the engine is carved
   // from this device's static scratch array (nothing allocated, nothing
   // freed); null for engines whose regions were allocated
@@ -298,6 +310,9 @@ amk_status check_executable(const amk_schedule& s) {
   const int64_t kmax = std::max({(int64_t)s.model.hidden, (int64_t)s.model.ffn,
                                  (int64_t)s.model.n_heads * s.model.head_dim});
   for (const Task& t : s.tasks) {
+    // a NOP task only waits and signals: accesses it declares are never made
+    if (t.type == AMK_TASK_NOP && !t.acc.empty())
+      return fail(AMK_ERR_UNSUPPORTED, "a NOP task declares memory accesses the kernel would not make");
     // a task's weight rows are addressed with 32-bit buffer offsets
     if (task_res_rows(t) * kmax * 2 + 4096 > ((int64_t)1 << 31))
       return fail(AMK_ERR_UNSUPPORTED, "a task's weight rows exceed 2 GiB");
@@ -399,6 +414,7 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
   e->model = m;
   e->config = c;
   e->device = dev;
+  e->multistep_ok = multistep_unsafe_task(*s) == -1;
   auto bail = [&](amk_status code) {
     free_engine(e);
     return code;
@@ -663,6 +679,9 @@ amk_status amk_decode_step(amk_engine* e, int32_t token, int32_t pos, void* stre
 amk_status amk_decode_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n_steps, int32_t* tokens_out,
                             void* stream) {
   if (!tokens_out) return fail(AMK_ERR_INVALID_ARG, "null tokens_out");
+  if (e && !e->multistep_ok)
+    return fail(AMK_ERR_UNSUPPORTED, "the engine's schedule fails amk_multistep_check: a multi-step launch could "
+                                     "start a step while a task of the previous one still runs");
   return amk::launch_steps(e, token, pos, n_steps, tokens_out, stream);
 }
 
@@ -767,9 +786,10 @@ amk_status amk_engine_steps(const amk_engine* e, int64_t* out) {
 }
 
 amk_status amk_stream_read_probe(const void* src, size_t bytes, float* out, int32_t blocks, void* stream) {
-  if (!src || !out || blocks < 1 || bytes % 16) return fail(AMK_ERR_INVALID_ARG, "bad probe arguments");
-  hipLaunchKernelGGL(amk_stream_read, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint4*>(src), (uint64_t)(bytes / 16), out);
+  if (!src || !out || blocks < 1 || bytes % 16 || bytes == 0 || bytes >= ((size_t)1 << 31))
+    return fail(AMK_ERR_INVALID_ARG, "bad probe arguments");
+  hipLaunchKernelGGL(amk_stream_read, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(src), (uint32_t)bytes, out);
   HIP_TRY(hipGetLastError());
   return AMK_OK;
 }

@@ -9,6 +9,8 @@ Five Llama-style decoders, batch 1:
             FFN 14336, vocab 128256, theta 5e5; 1024-token prompt, 256 steps
   8b_int8   8b with int8 per-output-row weights (fp32 scales), bf16
             activations at every projection input
+  8b_int8_a32  8b_int8's weights with fp32 projection inputs (a check of the
+            int8 path at the plain parity bar; not a benchmark workload)
   8b_int4   8b with int4 weights in groups of 128 (fp16 scale + zero),
             8192-token prompt, 128 decode steps
 
@@ -61,6 +63,10 @@ CONFIGS = {
                    False, 1024, 256, _ctx(1024, 256)),
     "8b_int8": Workload("8b_int8", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 500000.0, False,
                         "int8", True, 1024, 256, _ctx(1024, 256)),
+    # the same int8 weights with fp32 projection inputs (W8A32): the int8
+    # GEMV held to the plain parity bar, without the bf16 activation roundings
+    "8b_int8_a32": Workload("8b_int8_a32", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 500000.0, False,
+                            "int8", False, 1024, 256, _ctx(1024, 256)),
     "8b_int4": Workload("8b_int4", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 500000.0, False,
                         "int4", False, 8192, 128, _ctx(8192, 128)),
 }

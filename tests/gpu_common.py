@@ -6,14 +6,17 @@ Parity bar (per decode step): relative L2 error <= 1e-2 and max |g - o| <=
 
 Models whose projection inputs are rounded to bf16 (act_bf16, the W8A16
 reading of the int8 workload) are held to a bar derived from their measured
-conditioning instead: the oracle against itself, with every pre-rounding
-value perturbed by 1e-7 (fp32 roundoff), already differs by 1.2e-2 to 1.3e-2
-relative L2 on the 8B shape (the 1B-shape version of that measurement is
-pinned in test_oracle_conditioning.py).  The bar is three times that spread,
-4e-2 for both relative L2 and max-abs, and the argmax must agree unless the
-oracle's logit at the GPU's argmax is within that max-abs bound of the
-oracle's maximum (a tie at the conditioning floor, where either index is a
-correct result).
+conditioning instead (test_gpu_conditioning.py pins it on the full 8B int8
+model; test_oracle_conditioning.py the 1B-shape version on the CPU): the
+oracle against itself, with every value about to be rounded to bf16
+perturbed by a relative 1e-7 / 1e-6 (fp32 roundoff / the error of an fp32
+GEMV over thousands of terms), differs by up to 0.9e-2 / 1.5e-2 relative L2
+over three steps, against 1.4e-3 / 1.8e-3 for the same weights with fp32
+projection inputs.  The GPU path measures 1.7e-2 mean, 2.0e-2 worst over 32
+steps.  The bar is 4e-2 for both relative L2 and max-abs (2.6x the 1e-6
+spread), and the argmax must agree unless the oracle's logit at the GPU's
+argmax is within ACT_BF16_TIE * max|o| of the oracle's maximum (a tie at the
+conditioning floor, where either index is a correct result).
 """
 import sys
 
@@ -26,6 +29,9 @@ REL_L2 = 1e-2
 MAX_ABS = 2e-2
 ARGMAX = 0.99
 ACT_BF16_TOL = 4e-2
+# argmax tie window of act_bf16 models, as a fraction of max|oracle logit|:
+# about the measured conditioning spread (test_gpu_conditioning.py)
+ACT_BF16_TIE = 1.5e-2
 
 
 def log(msg):
@@ -74,7 +80,7 @@ def compare(got, want, tie_tol=0.0):
 
 def bars(wl):
     """(rel_l2, max_abs, tie) parity bar of a workload."""
-    return (ACT_BF16_TOL, ACT_BF16_TOL, ACT_BF16_TOL) if wl.act_bf16 else (REL_L2, MAX_ABS, 0.0)
+    return (ACT_BF16_TOL, ACT_BF16_TOL, ACT_BF16_TIE) if wl.act_bf16 else (REL_L2, MAX_ABS, 0.0)
 
 
 def check_run(results, min_argmax=ARGMAX, wl=None):
@@ -88,8 +94,9 @@ def check_run(results, min_argmax=ARGMAX, wl=None):
     return agree, worst_rel, worst_abs
 
 
-def teacher_forced(wl, weights, toks, compare_from=0, kv_prefix=None, start=0, sched=None):
-    """Run positions start.. over toks on both sides; compare steps >= compare_from."""
+def teacher_forced(wl, weights, toks, compare_from=0, kv_prefix=None, start=0, sched=None, progress=0):
+    """Run positions start.. over toks on both sides; compare steps >= compare_from.
+    progress > 0: log a line every `progress` steps (long runs)."""
     eng = make_engine(wl, weights, sched)
     orc = oracle.Model(wl, weights)
     kv_o = orc.new_kv() if kv_prefix is None else kv_prefix.copy()
@@ -104,4 +111,6 @@ def teacher_forced(wl, weights, toks, compare_from=0, kv_prefix=None, start=0, s
         o = orc.step(kv_o, tok, pos)
         if pos >= compare_from:
             results.append(compare(g, o, bars(wl)[2]))
+        if progress and (i + 1) % progress == 0:
+            log(f"  {wl.name}: step {i + 1}/{len(toks)} (position {pos})")
     return results, eng, kv_o

@@ -122,3 +122,54 @@ def test_last_position_and_rewind(tiny):
         rel, mab, same = compare(g, o)
         assert rel <= 1e-2 and mab <= 2e-2 and same, (r + i, rel)
     eng.close()
+
+
+def test_engine_refuses_unexecutable_nops_and_unsafe_multistep(tiny):
+    """A schedule that passes the gate but fails amk_multistep_check (a late
+    copy of a last-layer QKV task after an LM-head task) decodes single steps
+    correctly and refuses amk_decode_steps before launching; a NOP task that
+    declares an access (which the kernel would never make) is refused at
+    engine creation."""
+    import torch
+
+    from tests.test_multistep_check import _append
+    wl, w = tiny
+    m = amk.ModelConfig.from_workload(wl)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = lowered(m, num_cus=cus)
+    L = wl.n_layers
+    src = max(i for i, t in enumerate(s["tasks"]) if t["type"] == amk.TASK_QKV and t["p"][0] == L - 1)
+    q = next(c for c, qq in enumerate(s["queues"]) if qq and s["tasks"][qq[-1]]["type"] == amk.TASK_LMHEAD)
+    late = _append(s, {k: (list(v) if isinstance(v, list) else v) for k, v in s["tasks"][src].items()}, q)
+    late["tasks"][-1]["waits"], late["tasks"][-1]["sigs"] = [], []
+    late["model"] = m
+    late["config"] = amk.default_schedule_config(m, cus)
+    sch = amk.Schedule.from_dict(late)
+    assert sch.validate()[0] == 0
+    assert sch.multistep_check()[0] == amk.ERR_UNSUPPORTED
+    dev_w = amk.upload_model(m, w)
+    kv, logits = amk.alloc_state(m)
+    eng = amk.Engine(sch, dev_w, kv, logits)
+    toks = synth.tokens(2, 4, wl.vocab)
+    orc = oracle.Model(wl, w)
+    kv_o = orc.new_kv()
+    for p, tok in enumerate(toks):
+        rel, mab, ok = compare(gpu_step(eng, int(tok), p), orc.step(kv_o, int(tok), p))
+        assert rel <= 1e-2 and mab <= 2e-2 and ok
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    expect_status(amk.ERR_UNSUPPORTED, eng.decode_steps, int(toks[-1]), len(toks), 2, out)
+    eng.close()
+    sch.close()
+    # a NOP declaring a logits write after an LM-head task: the gate accepts
+    # it, the engine does not
+    lm = s["queues"][q][-1]
+    wacc = [a for a in s["tasks"][lm]["acc"] if a[1] == amk.ACCESS_WRITE][0]
+    nop = _append(s, {"type": amk.TASK_NOP, "p": [0] * 8, "waits": [], "sigs": [], "acc": [wacc]}, q)
+    nop["model"] = m
+    nop["config"] = amk.default_schedule_config(m, cus)
+    sch = amk.Schedule.from_dict(nop)
+    assert sch.validate()[0] == 0
+    expect_status(amk.ERR_UNSUPPORTED, amk.Engine, sch, dev_w, kv, logits)
+    sch.close()
+    orc.close()
+    log("engine: late QKV copy decodes single steps, refuses multi-step; NOP with accesses refused")

@@ -1,7 +1,8 @@
 """Greedy multi-step decode in one launch (amk_decode_steps) on MI355X: the
 device-side argmax and token feedback give the same tokens and bit-identical
 logits as one launch per step with the argmax taken on the host, and the
-oracle, fed the same tokens, agrees on the logits."""
+oracle, decoding greedily on its own from the same prompt, chooses the same
+tokens and agrees on the last step's logits."""
 import numpy as np
 import pytest
 
@@ -36,6 +37,24 @@ def _host_loop(eng, tok, pos, n):
     return toks, lg.copy()
 
 
+def _oracle_greedy(wl, w, prompt, p0, n, kv_prefix=None):
+    """The oracle's own greedy decode: prompt[:p0] (or a KV prefix of p0
+    rows) then n steps starting from prompt[p0], each next token the argmax
+    of the oracle's logits (lowest index on ties).  (tokens, last logits)."""
+    orc = oracle.Model(wl, w)
+    kv = orc.new_kv() if kv_prefix is None else kv_prefix.copy()
+    if kv_prefix is None:
+        for i in range(p0):
+            orc.step(kv, int(prompt[i]), i)
+    tok, toks = int(prompt[p0]), []
+    for i in range(n):
+        o = orc.step(kv, tok, p0 + i)
+        tok = int(np.argmax(o))
+        toks.append(tok)
+    orc.close()
+    return toks, o
+
+
 @pytest.mark.parametrize("sync_mode", [1, 0])
 def test_multistep_matches_host_loop_and_oracle(sync_mode):
     import torch
@@ -57,16 +76,13 @@ def test_multistep_matches_host_loop_and_oracle(sync_mode):
     dev_toks = out.cpu().numpy().tolist()
     assert dev_toks == host_toks, (dev_toks, host_toks)
     assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), host_logits.view(np.uint32))
-    # the oracle, teacher-forced on the same tokens, agrees at every step
-    orc = oracle.Model(wl, w)
-    kv = orc.new_kv()
-    seq = [int(t) for t in prompt] + dev_toks[:-1]
-    for i, t in enumerate(seq):
-        o = orc.step(kv, t, i)
+    # the oracle decodes greedily on its own from the same prompt
+    orc_toks, o = _oracle_greedy(wl, w, prompt, p0, n)
+    assert orc_toks == dev_toks, (orc_toks, dev_toks)
     rel, mab, same = compare(host_logits.astype(np.float64), o, bars(wl)[2])
     assert rel <= bars(wl)[0] and mab <= bars(wl)[1] and same, (rel, mab)
-    assert int(np.argmax(o)) == dev_toks[-1]
-    log(f"multistep sync_mode {sync_mode}: {n} tokens identical, final relL2 {rel:.2e}")
+    log(f"multistep sync_mode {sync_mode}: {n} tokens identical to the host loop and the oracle, "
+        f"final relL2 {rel:.2e}")
     for e, s in ((a, sa), (b, sb)):
         e.close()
         s.close()
@@ -79,10 +95,10 @@ def test_multistep_full_size_and_errors():
     wl = synth.get("8b")
     w = synth.model_weights(wl, seed=1)
     P = 1024
-    kvp = torch.from_numpy(synth.kv_prefix(wl, P, seed=3).view(np.int16).reshape(-1)).cuda()
+    kvp_host = synth.kv_prefix(wl, P, seed=3)
+    kvp = torch.from_numpy(kvp_host.view(np.int16).reshape(-1)).cuda()
     a, sa = _engine(wl, w)
     b, sb = _engine(wl, w)
-    del w
     for e in (a, b):
         e.kv_cache.copy_(kvp)
         e.set_kv_length(P)
@@ -94,12 +110,20 @@ def test_multistep_full_size_and_errors():
     b.check()
     assert out.cpu().numpy().tolist() == host_toks
     assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), host_logits.view(np.uint32))
+    # the oracle's own greedy decode after the same KV prefix: same tokens,
+    # and the last step's logits within the parity bar
+    orc_toks, o = _oracle_greedy(wl, w, np.array([0] * P + [7]), P, n, kv_prefix=kvp_host)
+    del w, kvp_host
+    assert orc_toks == host_toks, (orc_toks, host_toks)
+    rel, mab, same = compare(host_logits.astype(np.float64), o)
+    assert rel <= bars(wl)[0] and mab <= bars(wl)[1] and same, (rel, mab)
     for args, code in (((7, P, 0, out), amk.ERR_OUT_OF_RANGE), ((7, wl.max_ctx - 2, 4, out), amk.ERR_OUT_OF_RANGE),
                        ((7, P + n + 1, 2, out), amk.ERR_INVALID_ARG)):
         with pytest.raises(amk.AmkError) as e:
             b.decode_steps(*args)
         assert e.value.status == code
-    log(f"8b: {n} greedy steps in one launch match the host loop: {host_toks}")
+    log(f"8b: {n} greedy steps in one launch match the host loop and the oracle: {host_toks}, "
+        f"last-step relL2 {rel:.2e}")
     for e, s in ((a, sa), (b, sb)):
         e.close()
         s.close()
@@ -115,10 +139,17 @@ def test_region_stats_account_for_the_traced_launch():
     eng, sched = _engine(wl, w)
     with pytest.raises(amk.AmkError):
         eng.region_stats()  # tracing never enabled
-    eng.set_trace(True)
     eng.decode_step(3, 0)
     torch.cuda.synchronize()
     eng.check()
+    untraced = eng.logits.cpu().numpy().copy()
+    eng.set_trace(True)
+    eng.decode_step(3, 0)  # the same step again (rewind), traced
+    torch.cuda.synchronize()
+    eng.check()
+    # timing does not change what is timed: the traced launch's logits are
+    # bit-identical to the untraced launch's
+    assert np.array_equal(eng.logits.cpu().numpy().view(np.uint32), untraced.view(np.uint32))
     view = sched.view()
     stats = eng.region_stats()
     counts = {}
@@ -156,6 +187,11 @@ def test_multistep_to_the_last_position_and_single_step_equivalence():
     b.check()
     assert out.cpu().numpy().tolist() == host_toks
     assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), host_logits.view(np.uint32))
+    # the oracle's own greedy decode from the same prompt (1, 2, 3, 4, then 9)
+    orc_toks, o = _oracle_greedy(wl, w, np.array([1, 2, 3, 4, 9]), p0, n)
+    assert orc_toks == host_toks, (orc_toks, host_toks)
+    rel, mab, same = compare(host_logits.astype(np.float64), o)
+    assert rel <= bars(wl)[0] and mab <= bars(wl)[1] and same, (rel, mab)
     # rewind and take one step through each entry point
     one = torch.zeros(1, dtype=torch.int32, device="cuda")
     a.decode_step(5, p0)

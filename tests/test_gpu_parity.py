@@ -140,15 +140,29 @@ def test_schedule_knobs_keep_parity(sched):
 
 
 def test_tuner_keeps_only_safe_agreeing_faster_configs():
-    """The schedule tuner on the tiny decoder with a two-knob space: every kept
-    step passed the gate and reproduced the reference logits."""
+    """The schedule tuner on the tiny decoder with a three-knob space and the
+    oracle's logits of its check steps as the CPU reference: the library
+    default and every kept candidate passed the gate and matched both the
+    CPU reference and the default schedule's logits; a reference that is
+    off (scaled logits) makes the tuner refuse to start."""
+    from oracle.reference import check_step_logits
     from persistent_megakernel_wg_amd import tune
-    res = tune.tune(synth.get("tiny"), steps=8, space=[("attn_splits", [1, 2]), ("pipeline_depth", [4, 16])])
-    assert res["history"][0]["kept"]
+    wl = synth.get("tiny")
+    ref = check_step_logits(wl, synth.model_weights(wl, seed=1), 3)
+    res = tune.tune(wl, steps=8, space=[("attn_splits", [1, 2]), ("pipeline_depth", [4, 16]), ("sync_mode", [0])],
+                    reference=ref)
+    assert res["cpu_reference"]
+    h0 = res["history"][0]
+    assert h0["kept"] and h0["cpu_ok"] and h0["cpu_rel_l2"] <= 1e-2
+    measured = [h for h in res["history"][1:] if "error" not in h]
+    assert measured and all("cpu_rel_l2" in h for h in measured)
     for h in res["history"][1:]:
         if h.get("kept"):
-            assert h["parity"] and "error" not in h
-    log(f"tuner tiny: best {res['best']} {res['ms']:.4f} ms vs {res['reference_ms']:.4f} ms")
+            assert h["parity"] and h["cpu_ok"] and h["cpu_rel_l2"] <= 1e-2
+    log(f"tuner tiny: best {res['best']} {res['ms']:.4f} ms vs {res['reference_ms']:.4f} ms; "
+        f"cpu relL2 of candidates {[round(h['cpu_rel_l2'], 9) for h in measured]}")
+    with pytest.raises(RuntimeError, match="CPU reference"):
+        tune.tune(wl, steps=4, space=[], xcd_rounds=0, reference=[r * 1.1 for r in ref])
 
 
 @pytest.mark.parametrize("name", ["8b", "8b_int4"])
