@@ -398,6 +398,122 @@ def test_model_brute_force_tiny(tied):
         assert rel < 1e-5, (pos, rel)
 
 
+def bf16_round_f64(x):
+    """Round-to-nearest-even of float64 values to bf16 (8 significant bits),
+    straight from the double (normal range): x = m * 2^e, m in [0.5, 1)."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def np_dequant(wbits, fmt):
+    """The stored weights of one projection as exact float64 values, from the
+    format definitions (independent of the oracle's quantisers): bf16 as
+    stored; int8 one fp32 scale per output row, s = amax / 127, q =
+    clamp(rne(w / s), -127, 127) (all-zero rows: s = 1, q = 0); int4 groups of
+    128 inputs, s = fp16((max - min) / 15) (1 if 0), z = clamp(rne(-min / s),
+    0, 15), q = clamp(rne(w / s) + z, 0, 15), value (q - z) s.  The quantiser
+    arithmetic is fp32, rounding half to even."""
+    w = bf16_vals(wbits)
+    if fmt == "bf16":
+        return w
+    w32 = w.astype(np.float32)
+    if fmt == "int8":
+        amax = np.max(np.abs(w32), axis=1)
+        s = np.where(amax == 0, np.float32(1), amax / np.float32(127)).astype(np.float32)
+        q = np.clip(np.rint(w32 / s[:, None]), -127, 127)
+        q[amax == 0] = 0
+        return q.astype(np.float64) * s.astype(np.float64)[:, None]
+    rows, cols = w32.shape
+    g = w32.reshape(rows, cols // 128, 128)
+    mn, mx = g.min(axis=2), g.max(axis=2)
+    s = ((mx - mn) / np.float32(15)).astype(np.float16).astype(np.float32)
+    s = np.where(s == 0, np.float32(1), s)
+    z = np.clip(np.rint(-mn / s), 0, 15).astype(np.float32)
+    q = np.clip(np.rint(g / s[..., None]) + z[..., None], 0, 15)
+    return ((q - z[..., None]).astype(np.float64) * s[..., None].astype(np.float64)).reshape(rows, cols)
+
+
+def brute_force_decode_fmt(wl, w, toks):
+    """brute_force_decode for any weight format and for bf16 projection
+    inputs (act_bf16): the 7 projections of every layer and the LM head are
+    quantised and dequantised by np_dequant; with act_bf16 the inputs of
+    every projection (h, o, h2, a, the final normed x) are rounded to bf16;
+    K and V rows are rounded to bf16 from the double."""
+    L, H, hd, nq, nkv = wl.n_layers, wl.hidden, wl.head_dim, wl.n_heads, wl.n_kv_heads
+    rb = bf16_round_f64 if wl.act_bf16 else (lambda v: v)
+    E = bf16_vals(w[0])
+    lm = np_dequant(w[0] if wl.tied else w[2 + 9 * L], "bf16" if wl.tied else wl.wfmt)
+    Wl = [{k: (bf16_vals(w[lid(l, k)]) if k in (0, 5) else np_dequant(w[lid(l, k)], wl.wfmt)) for k in range(9)}
+          for l in range(L)]
+    Kc = [[] for _ in range(L)]
+    Vc = [[] for _ in range(L)]
+    out = []
+    for pos, tok in enumerate(toks):
+        x = E[tok].copy()
+        for l in range(L):
+            W = Wl[l]
+            h = rb(np_rms(x, W[0]))
+            q = (W[1] @ h).reshape(nq, hd)
+            k = (W[2] @ h).reshape(nkv, hd)
+            v = (W[3] @ h).reshape(nkv, hd)
+            q = np.stack([rope_complex(r, pos, wl.rope_theta) for r in q])
+            k = np.stack([rope_complex(r, pos, wl.rope_theta) for r in k])
+            Kc[l].append(bf16_round_f64(k))
+            Vc[l].append(bf16_round_f64(v))
+            K = np.repeat(np.stack(Kc[l], axis=1), nq // nkv, axis=0)
+            V = np.repeat(np.stack(Vc[l], axis=1), nq // nkv, axis=0)
+            S = np.einsum("hd,hjd->hj", q, K) / math.sqrt(hd)
+            Pm = np.exp(S - S.max(axis=1, keepdims=True))
+            Pm /= Pm.sum(axis=1, keepdims=True)
+            o = rb(np.einsum("hj,hjd->hd", Pm, V).reshape(-1))
+            x = x + W[4] @ o
+            h2 = rb(np_rms(x, W[5]))
+            gg, uu = W[6] @ h2, W[7] @ h2
+            x = x + W[8] @ rb(gg / (1 + np.exp(-gg)) * uu)
+        out.append(lm @ rb(np_rms(x, bf16_vals(w[1 + 9 * L]))))
+    return out
+
+
+def test_bf16_round_f64_points():
+    # halfway cases round to even, checked against the bit-level rounding
+    for v in (1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -(1.0 + 2.0**-8), 3.0 + 2.0**-7, 0.1, -7.3e-3, 0.0):
+        assert bf16_round_f64(v) == bf16_vals(np.array([oracle.round_bf16(v)], dtype=np.uint16))[0], v
+
+
+@pytest.mark.parametrize("fmt,act_bf16", [("bf16", True), ("int8", False), ("int8", True), ("int4", False),
+                                          ("int4", True)])
+def test_model_brute_force_quantised_and_act_bf16(fmt, act_bf16):
+    """Every projection of every layer quantised (non-zero random layers and
+    non-unit gains), with or without bf16 projection inputs: the oracle
+    equals the float64 brute force built from the format definitions (a
+    dropped or misplaced rounding of h, o, h2, a or the final normed x, or a
+    wrong dequantisation in any layer, moves the logits by far more than the
+    bound)."""
+    wl = TINY.with_(hidden=128, head_dim=32, ffn=256, n_layers=2, wfmt=fmt, act_bf16=act_bf16)
+    w = rand_weights(wl, 31)
+    for l in range(wl.n_layers):
+        for k in (0, 5):
+            w[lid(l, k)] = f32_to_bf16_bits(1.0 + 0.25 * rng.standard_normal(wl.hidden))
+    w[1 + 9 * wl.n_layers] = f32_to_bf16_bits(1.0 + 0.25 * rng.standard_normal(wl.hidden))
+    toks = [5, 77, 5, 299, 0, 123]
+    m = oracle.Model(wl, w)
+    kv = m.new_kv()
+    want = brute_force_decode_fmt(wl, w, toks)
+    for pos, tok in enumerate(toks):
+        got = m.step(kv, tok, pos)
+        rel = np.linalg.norm(got - want[pos]) / np.linalg.norm(want[pos])
+        assert rel < 1e-9, (fmt, act_bf16, pos, rel)
+    # the same weights without the activation rounding give clearly other
+    # logits (the rounding is there), and the quantised model differs from
+    # the bf16 one (the quantisation is applied)
+    if act_bf16:
+        other = brute_force_decode_fmt(wl.with_(act_bf16=False), w, toks)[-1]
+        assert np.linalg.norm(other - want[-1]) / np.linalg.norm(want[-1]) > 1e-4
+    if fmt != "bf16":
+        other = brute_force_decode_fmt(wl.with_(wfmt="bf16"), w, toks)[-1]
+        assert np.linalg.norm(other - want[-1]) / np.linalg.norm(want[-1]) > 1e-3
+
+
 def test_model_quantised_uses_dequantised_weights():
     """An int8 (resp. int4) model equals the bf16 oracle run on the
     explicitly dequantised weights (written back as exact doubles via a
