@@ -165,6 +165,27 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kRowBcast31, 0xC>(v, v));
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// the value of lane (lane ^ OFF), OFF = 8, 16 or 32, on the VALU: a row
+// rotation by 8 within each 16-lane row, or the row-pair / half-wave swaps
+// (the swap returns the two operands with odd rows (upper half) of the first
+// and even rows (lower half) of the second exchanged; each lane takes the
+// one that holds its partner)
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (OFF == 8) {
+    return dpp<kRowRor8>(v, v);
+  } else if constexpr (OFF == 16) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((opaque_tid() & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(OFF == 32, "lane_xor: OFF is 8, 16 or 32");
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((opaque_tid() & 32) ? r[0] : r[1]);
+  }
+}
+
 // sum over groups of LG consecutive lanes (LG = 8, 16, 32 or 64), every lane
 // of a group gets its group's sum
 template <int LG>
@@ -173,7 +194,7 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LG == 16) return row_sum16(v);
   if constexpr (LG == 32) {
     v = row_sum16(v);
-    return v + __shfl_xor(v, 16, 64);
+    return v + lane_xor<16>(v);
   }
   if constexpr (LG == 64) return wave_sum(v);
   return v;
@@ -486,13 +507,33 @@ constexpr int kAttnWaves = kWaves - 1;
 
 
 
-// Query heads one attention pass takes (task_attn): the group size rounded
-// up to a power of two, at most 64 lanes / (head_dim / 8 lanes per row)
-// heads; larger groups take several passes.  The engine sizes the
-// attention scratch in LDS for this width.
-__host__ __device__ constexpr int attn_pass_heads(int grp, int hd) {
+// Attention splits of at least kAttnPmMin positions take the position-major
+// lane layout (every 16-byte load brings distinct rows, so more bytes are in
+// flight per register), shorter ones the head-major layout (the heads of a
+// pass in parallel lane groups: a shorter chain per position, and q read
+// straight into registers).
+constexpr int kAttnPmMin = 128;
+
+// Query heads one pass takes.  Head-major: the group size rounded up to a
+// power of two, at most 64 lanes / (head_dim / 8 lanes per row).
+// Position-major: the group size rounded up to a power of two, at most 4
+// (every lane keeps q and the running sums of all heads of its pass in
+// registers).  Larger groups take several passes.
+__host__ __device__ constexpr int attn_pass_heads_hm(int grp, int hd) {
   return (grp == 1 ? 1 : grp == 2 ? 2 : grp <= 4 ? 4 : 8) < 512 / hd ? (grp == 1 ? 1 : grp == 2 ? 2 : grp <= 4 ? 4 : 8)
                                                                    : 512 / hd;
+}
+__host__ __device__ constexpr int attn_pass_heads_pm(int grp) { return grp == 1 ? 1 : grp == 2 ? 2 : 4; }
+
+// LDS floats of an attention pass (the engine sizes the attention scratch
+// for the larger of the two layouts).  Head-major: every lane's (acc[8],
+// max, sum), then the merged heads.  Position-major: q, the row at pos, the
+// waves' states and the merged heads.
+__host__ __device__ constexpr int attn_lds_floats(int grp, int hd) {
+  return (kWaves * 64 * 10 + attn_pass_heads_hm(grp, hd) * (hd + 2)) >
+                 (attn_pass_heads_pm(grp) * hd + 2 * hd + (kWaves + 1) * attn_pass_heads_pm(grp) * (hd + 2))
+             ? kWaves * 64 * 10 + attn_pass_heads_hm(grp, hd) * (hd + 2)
+             : attn_pass_heads_pm(grp) * hd + 2 * hd + (kWaves + 1) * attn_pass_heads_pm(grp) * (hd + 2);
 }
 
 // x for 16-byte chunks of E elements, staged so lane l of wave-load j reads
@@ -548,29 +589,56 @@ struct FmtInt8 {
 
 // int4 rows: a 16-byte chunk is 32 columns (a quarter group of 128) with the
 // group's {fp16 scale, fp16 zero}; word q holds columns 8q..8q+7, nibble j
-// column 2j and nibble j+4 column 2j+1.  Contribution s*(sum q x - z*sum x).
+// column 2j and nibble j+4 column 2j+1, so (word >> 4j) & 0x000F000F holds
+// the column pair (2j, 2j+1) in its two halves.  OR-ing in 0x4300 per half
+// makes the exact bf16 values 128 + q, which meet the staged input (bf16
+// high parts and bf16 remainders of x, packed in column pairs, see stage_x)
+// in the bf16 dot2 instruction:
+//   d = sum (128 + q) (xh + xl),  contribution s * (d - (z + 128) * sum (xh + xl)).
+// Three shifts, four and-ors and eight dot2 per 8 columns, where a convert
+// and an FMA per column cost 24.
 struct FmtInt4 {
   static constexpr int E = 32;
   static constexpr bool kMeta = true;
+  __device__ __forceinline__ static float dot2(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
+  }
   __device__ __forceinline__ static float dot(float acc, u32x4 w, uint32_t m, const float* xs, int cj, int lane,
                                               const float* csum) {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    float d = 0.0f;
+    // the mask and the bias as wave-uniform values rather than literals:
+    // the compiler then forms one three-operand and-or per pair (a VOP3
+    // instruction takes no literal on this target)
+    uint32_t kMask, kBias;
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(kMask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(kBias));
+    // four independent accumulation chains (the dot2 result latency is
+    // several issue slots; one chain per row would leave the SIMD idle)
+    float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // all eight input reads first, so their LDS latency overlaps
+    u32x4 xv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xv[k] = *reinterpret_cast<const u32x4*>(xs + ((cj * 8 + k) * 64 + lane) * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 xa = *reinterpret_cast<const float4*>(xs + ((cj * 8 + 2 * q) * 64 + lane) * 4);
-      const float4 xb = *reinterpret_cast<const float4*>(xs + ((cj * 8 + 2 * q + 1) * 64 + lane) * 4);
-      d = fmaf((float)((wd[q] >> 0) & 0xFu), xa.x, d);
-      d = fmaf((float)((wd[q] >> 16) & 0xFu), xa.y, d);
-      d = fmaf((float)((wd[q] >> 4) & 0xFu), xa.z, d);
-      d = fmaf((float)((wd[q] >> 20) & 0xFu), xa.w, d);
-      d = fmaf((float)((wd[q] >> 8) & 0xFu), xb.x, d);
-      d = fmaf((float)((wd[q] >> 24) & 0xFu), xb.y, d);
-      d = fmaf((float)((wd[q] >> 12) & 0xFu), xb.z, d);
-      d = fmaf((float)((wd[q] >> 28) & 0xFu), xb.w, d);
+      const u32x4 xh = xv[2 * q], xl = xv[2 * q + 1];
+      const uint32_t p0 = (wd[q] & kMask) | kBias;
+      const uint32_t p1 = ((wd[q] >> 4) & kMask) | kBias;
+      const uint32_t p2 = ((wd[q] >> 8) & kMask) | kBias;
+      const uint32_t p3 = ((wd[q] >> 12) & kMask) | kBias;
+      d[0] = dot2(p0, xh.x, d[0]);
+      d[1] = dot2(p0, xl.x, d[1]);
+      d[2] = dot2(p1, xh.y, d[2]);
+      d[3] = dot2(p1, xl.y, d[3]);
+      d[0] = dot2(p2, xh.z, d[0]);
+      d[1] = dot2(p2, xl.z, d[1]);
+      d[2] = dot2(p3, xh.w, d[2]);
+      d[3] = dot2(p3, xl.w, d[3]);
     }
     const float cs = csum[cj * 64 + lane];
-    return fmaf(f16_to_f(m & 0xFFFFu), d - f16_to_f(m >> 16) * cs, acc);
+    const float dd = (d[0] + d[2]) + (d[1] + d[3]);
+    return fmaf(f16_to_f(m & 0xFFFFu), dd - (f16_to_f(m >> 16) + 128.0f) * cs, acc);
   }
 };
 
@@ -590,13 +658,16 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
   const float eps = P.eps;
   const int act_bf16 = P.act_bf16;
   float ss = 0.0f;
-  // the gain of this thread's first two groups, read now so that its round
-  // trip overlaps the input's
+  // the gain of this thread's first two groups of 4 inputs (int4: of its
+  // first group of 8), read now so that its round trip overlaps the input's
+  constexpr bool G8 = F::E == 32;
   uint2 g2[2] = {{0u, 0u}, {0u, 0u}};
   if (NORM && reader)
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (tid + k * nr < n4) g2[k] = reinterpret_cast<const uint2*>(gain)[tid + k * nr];
+    for (int k = 0; k < 2; ++k) {
+      const int gi = G8 ? 2 * tid + k : tid + k * nr;
+      if (gi < n4) g2[k] = reinterpret_cast<const uint2*>(gain)[gi];
+    }
   if (tsrc) {  // up to 4 groups of 4 words per thread in flight at once
     TagSpin sp;
     for (int i0 = tid; reader && i0 < n4; i0 += nr * 4) {
@@ -635,6 +706,54 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
   if (NORM) inv = 1.0f / sqrtf(block_sum(ss, red) / (float)n + eps);
   else __syncthreads();
   float sx = 0.0f;
+  if constexpr (G8) {
+    // int4: per group of 8 inputs (one thread; the 4 groups of a chunk of 32
+    // in 4 adjacent lanes) the norm, then the split into bf16 high parts xh
+    // (4 column pairs, in the group's first slot) and the bf16 roundings xl
+    // of the remainders x - xh (second slot): xh + xl is exact in fp32 and
+    // within 2^-17 |x| of x.  csum is each chunk's sum of xh + xl, the
+    // values the dot products see (chunks wholly in the padding get 0).
+    const int n8 = n >> 3;
+    for (int g = tid; reader && g < n8; g += nr) {
+      float4* pa = reinterpret_cast<float4*>(xs + xperm_e<32>(8 * g));
+      float4* pb = reinterpret_cast<float4*>(xs + xperm_e<32>(8 * g + 4));
+      float4 a = *pa, b = *pb;
+      if (NORM) {
+        const uint2 ga = g == tid ? g2[0] : reinterpret_cast<const uint2*>(gain)[2 * g];
+        const uint2 gb = g == tid ? g2[1] : reinterpret_cast<const uint2*>(gain)[2 * g + 1];
+        a = make_float4(a.x * inv * bf16_lo(ga.x), a.y * inv * bf16_hi(ga.x), a.z * inv * bf16_lo(ga.y),
+                        a.w * inv * bf16_hi(ga.y));
+        b = make_float4(b.x * inv * bf16_lo(gb.x), b.y * inv * bf16_hi(gb.x), b.z * inv * bf16_lo(gb.y),
+                        b.w * inv * bf16_hi(gb.y));
+      }
+      if (act_bf16) {
+        a = make_float4(bf16_round(a.x), bf16_round(a.y), bf16_round(a.z), bf16_round(a.w));
+        b = make_float4(bf16_round(b.x), bf16_round(b.y), bf16_round(b.z), bf16_round(b.w));
+      }
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t hp[4], lp[4];
+      float t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hb[2], lb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          hb[e] = bf16_bits(v[2 * j + e]);
+          const float xh = __uint_as_float(hb[e] << 16);
+          lb[e] = bf16_bits(v[2 * j + e] - xh);
+          t += xh + __uint_as_float(lb[e] << 16);
+        }
+        hp[j] = hb[0] | (hb[1] << 16);
+        lp[j] = lb[0] | (lb[1] << 16);
+      }
+      *reinterpret_cast<u32x4*>(pa) = u32x4{hp[0], hp[1], hp[2], hp[3]};
+      *reinterpret_cast<u32x4*>(pb) = u32x4{lp[0], lp[1], lp[2], lp[3]};
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      if ((g & 3) == 0) csum[g >> 2] = t;
+    }
+    for (int c = (n >> 5) + tid; c < padded / 32; c += kThreads) csum[c] = 0.0f;
+  } else
   for (int i = tid; reader && i < n4; i += nr) {
     float4* p = reinterpret_cast<float4*>(xs + xperm_e<F::E>(i * 4));
     float4 v = *p;
@@ -654,17 +773,7 @@ __device__ __forceinline__ bool stage_x(const VmParams& P, const void* src, cons
     if (tid == 0) *xsum = tot;
   }
   __syncthreads();
-  if constexpr (F::E == 32) {
-    for (int c = tid; c < padded / 32; c += kThreads) {
-      float t = 0.0f;
-      for (int k = 0; k < 32; k += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(xs + xperm_e<32>(c * 32 + k));
-        t += v.x + v.y + v.z + v.w;
-      }
-      csum[c] = t;
-    }
-    __syncthreads();
-  }
+
   return true;
 }
 
@@ -1118,7 +1227,8 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
 }
 
 // ------------------------------------------------------------ attention --
-// One split [p0, p1) of the positions of kv head g, for query heads
+// Head-major layout (short splits): one split [p0, p1) of the positions of
+// kv head g, for query heads
 // h0..h0+nh-1 (nh <= GP).  Lane layout ("head rows"): LH = hd/8 lanes hold the
 // 8-element chunks of one row; GP groups of LH lanes take GP query heads; the
 // remaining factor PW = 64/(LH*GP) takes PW positions per wave step.  Chunk c
@@ -1130,7 +1240,7 @@ __device__ __forceinline__ bool task_gemv(const VmParams& P, TaskRef t, float* s
 // before the wait; the row at `pos` (written by this launch) is re-read after.
 // Output: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
 template <int LH, int GP, int MAXC>
-__device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, int g, int h0,
+__device__ __forceinline__ bool attn_split_hm(const VmParams& P, TaskRef t, int l, int g, int h0,
                                            int nh, int s, int S, int p0, int p1, float* smem) {
   constexpr int PW = 64 / (LH * GP);
   const int hd = P.hd, pos = P.pos, tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
@@ -1344,13 +1454,312 @@ __device__ __forceinline__ bool attn_split(const VmParams& P, TaskRef t, int l, 
 }
 
 template <int LH, int GP>
-__device__ __forceinline__ bool attn_heads(const VmParams& P, TaskRef t, int l, int g, int s, int S,
+__device__ __forceinline__ bool attn_heads_hm(const VmParams& P, TaskRef t, int l, int g, int s, int S,
                                            int p0, int p1, float* smem) {
   const int grp = P.nq / P.nkv;
   constexpr int MAXC = 4;
   for (int h0 = 0; h0 < grp; h0 += GP) {  // later passes find the counters reached
     if (h0 > 0) __syncthreads();
-    if (!attn_split<LH, GP, MAXC>(P, t, l, g, g * grp + h0, min(GP, grp - h0), s, S, p0, p1, smem))
+    if (!attn_split_hm<LH, GP, MAXC>(P, t, l, g, g * grp + h0, min(GP, grp - h0), s, S, p0, p1, smem))
+      return false;
+  }
+  return true;
+}
+
+// Position-major layout (long splits): one split [p0, p1) of the positions
+// of kv head g, for query heads h0..h0+nh-1 (nh <= GP).  Lane layout: LH =
+// hd/8 lanes hold the 8-element
+// chunks of one K/V row, so a wave step covers PW = 64/LH positions, and
+// every lane scores its row chunk against all GP query heads (a 16-byte load
+// brings distinct rows into all 64 lanes).  Chunk c of block b of attention
+// wave w is position p0 + ((b*MAXC + c)*naw + w)*PW + lane/LH.  A score needs
+// one LH-lane DPP sum; the online softmax and sum p*V stay in each lane
+// (every lane of a row group holds the group's max and sum per head); the
+// PW position groups of a wave merge through cross-lane exchanges, then the
+// waves once through LDS.  Rows of earlier positions were written by
+// previous launches, so blocks 0 and 1 are loaded before the wait; the row
+// at `pos` (written by this launch) is taken afterwards.  q (and, with
+// tagged activations, the row at pos) is staged once in LDS.
+// Output: part[(l*nq + h)*S + s] = {sum_j p_j V_j (hd values), max, sum p}.
+template <int LH, int GP, int MAXC>
+__device__ __forceinline__ bool attn_split_pm(const VmParams& P, TaskRef t, int l, int g, int h0,
+                                           int nh, int s, int S, int p0, int p1, float* smem) {
+  constexpr int PW = 64 / LH;
+  const int hd = P.hd, pos = P.pos, tid = opaque_tid(), lane = tid & 63;
+  const int pw = lane / LH, li = lane % LH;
+  int* flag = reinterpret_cast<int*>(smem + kWaves);
+  // K / V rows of (l, g) through buffer descriptors: 32-bit offsets, and
+  // positions past p1 read as zero without touching memory
+  const uint32_t rows_bytes = (uint32_t)P.mc * hd * 2;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.kv + (((int64_t)l * 2 + 0) * P.nkv + g) * P.mc * hd, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(P.kv + (((int64_t)l * 2 + 1) * P.nkv + g) * P.mc * hd, rows_bytes);
+  const uint32_t lane_off = (uint32_t)li * 16u, row_b = (uint32_t)hd * 2u;
+  // waves 1..7 take the positions; wave 0 polls and keeps no loads in flight
+  // (poll_mode 3: waves 0..kDmaWave0-1 take them, the DMA waves none)
+  const int wsc = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int aw0 = P.poll_late == 3 ? 0 : 1;
+  const int naw = P.poll_late == 3 ? kDmaWave0 : kAttnWaves;
+  const bool aw = wsc >= aw0 && wsc < aw0 + naw;  // this wave takes positions
+  const int wi = wsc - aw0;
+  auto posof = [&](int blk, int c) {
+    return p0 + ((blk * MAXC + c) * naw + wi) * PW + pw;
+  };
+  // first position of chunk c of block blk in this wave (the same in every lane)
+  auto chunk0 = [&](int blk, int c) { return __builtin_amdgcn_readfirstlane(posof(blk, c) - pw); };
+  auto koff = [&](int j, bool ok) { return ok ? (uint32_t)j * row_b + lane_off : kOob; };
+  // two register buffers of blocks: blocks 0 and 1 are loaded before the
+  // wait (positions before pos only: rows of earlier launches); later blocks
+  // are loaded into the buffer just consumed, two blocks ahead
+  u32x4 ka[MAXC], va[MAXC], kb[MAXC], vb[MAXC];
+  // a chunk that holds no position of the split: zeros, without a load (an
+  // out-of-range load would still take a turn in the address pipeline)
+  auto load_blk = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk, bool before_wait) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = posof(blk, c);
+      if (chunk0(blk, c) < p1) {
+        const uint32_t o = koff(j, j < p1 && (!before_wait || j < pos));
+        k[c] = bload(rk, o);
+        v[c] = bload(rv, o);
+      } else {
+        k[c] = u32x4{0u, 0u, 0u, 0u};
+        v[c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  if (aw) {
+    load_blk(ka, va, 0, true);
+    load_blk(kb, vb, 1, true);
+  }
+  if (!vm_wait(P, t, flag)) return false;
+  // LDS: q of the pass [GP][hd] (scaled), the row at pos [2][hd] (tagged
+  // mode), the waves' states [kWaves][GP][hd] + [kWaves][GP][2], and the
+  // merged outputs [GP][hd] + [GP][2]
+  float* qs = smem + P.lds_att;
+  float* kvs = qs + GP * hd;
+  float* wacc = kvs + 2 * hd;
+  float* wst = wacc + kWaves * GP * hd;
+  float* wout = wst + kWaves * GP * 2;
+  const float scale = 1.0f / sqrtf((float)hd);
+  const bool tagged = P.tagged != 0;
+  const int64_t qbase = (int64_t)l * P.nq * hd + (int64_t)h0 * hd;  // heads h0.. are contiguous
+  const bool has_pos = p0 <= pos && pos < p1;
+  const int nq_w = nh * hd;
+  if (tagged) {
+    // one round of reads by the input threads: q of the pass and, when the
+    // split holds pos, that row's K and V (the launch's tagged copy; no load
+    // of the cache reaches row pos)
+    const int nr = input_threads(P);
+    const int nw = nq_w + (has_pos ? 2 * hd : 0);
+    const int64_t kd = (P.tkv - P.tq) + (((int64_t)l * 2 + 0) * P.nkv + g) * hd - qbase;
+    const int64_t vd = (P.tkv - P.tq) + (((int64_t)l * 2 + 1) * P.nkv + g) * hd - qbase;
+    TagSpin sp;
+    float v[4];
+    auto idx = [&](int k) -> int64_t {
+      const int i = tid + k * nr;
+      return i < nq_w ? (int64_t)i : (i < nq_w + hd ? kd + (i - nq_w) : vd + (i - nq_w - hd));
+    };
+    if (tid < nr && ld_tagged<4>(P, P.tq + qbase, [&](int k) { return tid + k * nr < nw; }, idx, v, sp)) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid + k * nr;
+        if (i < nq_w) qs[i] = v[k] * scale;
+        else if (i < nw) kvs[i - nq_w] = v[k];
+      }
+    }
+    if (block_any(sp.failed, smem)) return false;
+    trace_mark(P, t, 1);
+  } else {
+    for (int i = tid; i < nq_w; i += kThreads) qs[i] = P.q[qbase + i] * scale;
+    __syncthreads();
+  }
+  float q[GP][8];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (h < nh) {
+      a = *reinterpret_cast<const float4*>(qs + h * hd + li * 8);
+      b = *reinterpret_cast<const float4*>(qs + h * hd + li * 8 + 4);
+    }
+    q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
+    q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
+  }
+  // the chunk (block pblk, chunk pc) of this lane whose position is pos
+  int pblk = -1, pc = 0;
+  {
+    const int d = pos - p0 - pw;
+    if (aw && has_pos && d >= 0 && d % PW == 0 && (d / PW) % naw == wi) {
+      const int bc = d / PW / naw;
+      pblk = bc / MAXC;
+      pc = bc % MAXC;
+    }
+  }
+  // the row at pos: tagged mode from LDS (bf16 values carried as floats),
+  // counter mode from the cache (visible after the acquire of the wait)
+  auto patch = [&](u32x4 (&k)[MAXC], u32x4 (&v)[MAXC], int blk) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (blk == pblk && c == pc) {
+        if (tagged) {
+          auto pk = [](const float* f) {
+            u32x4 r;
+            r.x = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+            r.y = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u);
+            r.z = (__float_as_uint(f[4]) >> 16) | (__float_as_uint(f[5]) & 0xFFFF0000u);
+            r.w = (__float_as_uint(f[6]) >> 16) | (__float_as_uint(f[7]) & 0xFFFF0000u);
+            return r;
+          };
+          k[c] = pk(kvs + li * 8);
+          v[c] = pk(kvs + hd + li * 8);
+        } else {
+          k[c] = bload(rk, koff(pos, true));
+          v[c] = bload(rv, koff(pos, true));
+        }
+      }
+  };
+  float M[GP], Ls[GP], acc[GP][8];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    M[h] = -INFINITY;
+    Ls[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  }
+  const int len = p1 - p0;
+  const int per_blk = MAXC * naw * PW;
+  const int nblk = aw ? (len + per_blk - 1) / per_blk : 0;
+  auto compute = [&](const u32x4 (&kr)[MAXC], const u32x4 (&vr)[MAXC], int blk) {
+    float sc[MAXC][GP];
+    float bm[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) bm[h] = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) sc[c][h] = -INFINITY;
+      if (chunk0(blk, c) >= p1) continue;  // no position of the split in this chunk
+      const u32x4 k8 = kr[c];
+      const float kf[8] = {bf16_lo(k8.x), bf16_hi(k8.x), bf16_lo(k8.y), bf16_hi(k8.y),
+                           bf16_lo(k8.z), bf16_hi(k8.z), bf16_lo(k8.w), bf16_hi(k8.w)};
+      const bool valid = posof(blk, c) < p1;
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        float d = q[h][0] * kf[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) d = fmaf(q[h][e], kf[e], d);
+        d = group_sum<LH>(d);
+        sc[c][h] = valid ? d : -INFINITY;
+        bm[h] = fmaxf(bm[h], sc[c][h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float nm = fmaxf(M[h], bm[h]);
+      const float alpha = M[h] == -INFINITY ? 0.0f : __expf(M[h] - nm);
+      Ls[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+      M[h] = nm;
+    }
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      if (chunk0(blk, c) >= p1) continue;
+      const u32x4 v8 = vr[c];
+      const float vf[8] = {bf16_lo(v8.x), bf16_hi(v8.x), bf16_lo(v8.y), bf16_hi(v8.y),
+                           bf16_lo(v8.z), bf16_hi(v8.z), bf16_lo(v8.w), bf16_hi(v8.w)};
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float p = sc[c][h] == -INFINITY ? 0.0f : __expf(sc[c][h] - M[h]);
+        Ls[h] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    patch(ka, va, blk);
+    compute(ka, va, blk);
+    if (blk + 2 < nblk) load_blk(ka, va, blk + 2, tagged);
+    if (blk + 1 < nblk) {
+      patch(kb, vb, blk + 1);
+      compute(kb, vb, blk + 1);
+      if (blk + 3 < nblk) load_blk(kb, vb, blk + 3, tagged);
+    }
+  }
+  // merge the PW position groups of the wave (lanes pw, pw ^ 1, ...): both
+  // partners form the same sums, so every lane ends with the wave's state
+  auto merge_lanes = [&](auto xr) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float mo = xr(M[h]);
+      const float lo = xr(Ls[h]);
+      const float nm = fmaxf(M[h], mo);
+      const float fa = M[h] == -INFINITY ? 0.0f : __expf(M[h] - nm);
+      const float fb = mo == -INFINITY ? 0.0f : __expf(mo - nm);
+      Ls[h] = Ls[h] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * fa + xr(acc[h][e]) * fb;
+      M[h] = nm;
+    }
+  };
+  if constexpr (LH <= 8) merge_lanes([](float v) { return lane_xor<8>(v); });
+  if constexpr (LH <= 16) merge_lanes([](float v) { return lane_xor<16>(v); });
+  merge_lanes([](float v) { return lane_xor<32>(v); });
+  // then the waves through LDS (lanes of position group 0 write)
+  if (pw == 0) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      float* o = wacc + (wsc * GP + h) * hd + li * 8;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      if (li == 0) {
+        wst[(wsc * GP + h) * 2] = M[h];
+        wst[(wsc * GP + h) * 2 + 1] = Ls[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * hd; i += kThreads) {
+    const int hq = i / hd, e = i - hq * hd;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, wst[(w * GP + hq) * 2]);
+    float o = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wst[(w * GP + hq) * 2];
+      const float f = mw == -INFINITY ? 0.0f : __expf(mw - mt);
+      o = fmaf(f, wacc[(w * GP + hq) * hd + e], o);
+      lsum = fmaf(f, wst[(w * GP + hq) * 2 + 1], lsum);
+    }
+    wout[i] = o;
+    if (e == 0) {
+      wout[GP * hd + hq * 2] = mt;
+      wout[GP * hd + hq * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  const int EW = tagged ? kThreads : epilogue_threads(P);
+  if (tid < EW) {  // the releasing threads store everything other workgroups read
+    for (int i = tid; i < nh * (hd + 2); i += EW) {
+      const int hq = i / (hd + 2), e = i - hq * (hd + 2);
+      const float v = e < hd ? wout[hq * hd + e] : wout[GP * hd + hq * 2 + (e - hd)];
+      const int64_t o = (((int64_t)l * P.nq + h0 + hq) * S + s) * (hd + 2) + e;
+      if (tagged) st_tag(P.tpart + o, v, P.tag);
+      else st_agent(P.part + o, v);
+    }
+  }
+  return true;
+}
+
+template <int LH, int GP>
+__device__ __forceinline__ bool attn_heads_pm(const VmParams& P, TaskRef t, int l, int g, int s, int S,
+                                           int p0, int p1, float* smem) {
+  const int grp = P.nq / P.nkv;
+  constexpr int MAXC = 4;
+  for (int h0 = 0; h0 < grp; h0 += GP) {  // later passes find the counters reached
+    if (h0 > 0) __syncthreads();
+    if (!attn_split_pm<LH, GP, MAXC>(P, t, l, g, g * grp + h0, min(GP, grp - h0), s, S, p0, p1, smem))
       return false;
   }
   return true;
@@ -1374,21 +1783,37 @@ __device__ __forceinline__ bool task_attn(const VmParams& P, TaskRef t, float* s
         else st_agent(P.part + o, e == hd ? -INFINITY : 0.0f);
       }
   } else {
-    // GP = heads per pass (attn_pass_heads)
-    const int gp = attn_pass_heads(grp, hd);
     bool ok;
-    if (hd == 64) {
-      ok = gp == 1 ? attn_heads<8, 1>(P, t, l, g, s, S, p0, p1, smem)
-         : gp == 2 ? attn_heads<8, 2>(P, t, l, g, s, S, p0, p1, smem)
-         : gp == 4 ? attn_heads<8, 4>(P, t, l, g, s, S, p0, p1, smem)
-                   : attn_heads<8, 8>(P, t, l, g, s, S, p0, p1, smem);
-    } else if (hd == 128) {
-      ok = gp == 1 ? attn_heads<16, 1>(P, t, l, g, s, S, p0, p1, smem)
-         : gp == 2 ? attn_heads<16, 2>(P, t, l, g, s, S, p0, p1, smem)
-                   : attn_heads<16, 4>(P, t, l, g, s, S, p0, p1, smem);
-    } else {
-      ok = gp == 1 ? attn_heads<32, 1>(P, t, l, g, s, S, p0, p1, smem)
-                   : attn_heads<32, 2>(P, t, l, g, s, S, p0, p1, smem);
+    if (p1 - p0 >= kAttnPmMin) {  // position-major, GP = attn_pass_heads_pm
+      const int gp = attn_pass_heads_pm(grp);
+      if (hd == 64) {
+        ok = gp == 1 ? attn_heads_pm<8, 1>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 2 ? attn_heads_pm<8, 2>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_pm<8, 4>(P, t, l, g, s, S, p0, p1, smem);
+      } else if (hd == 128) {
+        ok = gp == 1 ? attn_heads_pm<16, 1>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 2 ? attn_heads_pm<16, 2>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_pm<16, 4>(P, t, l, g, s, S, p0, p1, smem);
+      } else {
+        ok = gp == 1 ? attn_heads_pm<32, 1>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 2 ? attn_heads_pm<32, 2>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_pm<32, 4>(P, t, l, g, s, S, p0, p1, smem);
+      }
+    } else {  // head-major, GP = attn_pass_heads_hm
+      const int gp = attn_pass_heads_hm(grp, hd);
+      if (hd == 64) {
+        ok = gp == 1 ? attn_heads_hm<8, 1>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 2 ? attn_heads_hm<8, 2>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 4 ? attn_heads_hm<8, 4>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_hm<8, 8>(P, t, l, g, s, S, p0, p1, smem);
+      } else if (hd == 128) {
+        ok = gp == 1 ? attn_heads_hm<16, 1>(P, t, l, g, s, S, p0, p1, smem)
+           : gp == 2 ? attn_heads_hm<16, 2>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_hm<16, 4>(P, t, l, g, s, S, p0, p1, smem);
+      } else {
+        ok = gp == 1 ? attn_heads_hm<32, 1>(P, t, l, g, s, S, p0, p1, smem)
+                     : attn_heads_hm<32, 2>(P, t, l, g, s, S, p0, p1, smem);
+      }
     }
     if (!ok) return false;
   }

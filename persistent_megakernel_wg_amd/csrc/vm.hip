@@ -430,11 +430,10 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
     const int64_t padded = (K + E * 64 - 1) / (E * 64) * (E * 64);
     return (padded + padded / 32 + 3) / 4 * 4;
   };
-  // attention: per-lane (acc[8], max, sum) of every thread, then the pass's
-  // merged heads ([GP][hd] outputs + [GP][2] stats); merge: [S][hd + 1]
-  const int64_t gp_max = attn_pass_heads(m.n_heads / m.n_kv_heads, (int)hd);
+  // attention: the larger of the two lane layouts' scratch
+  // (attn_lds_floats); merge: [S][hd + 1]
   const int64_t att_floats =
-      std::max<int64_t>(kWaves * 64 * 10 + gp_max * (hd + 2), (int64_t)c.attn_splits * (hd + 1));
+      std::max<int64_t>(attn_lds_floats(m.n_heads / m.n_kv_heads, (int)hd), (int64_t)c.attn_splits * (hd + 1));
   const int64_t lds_att = kHead;
   auto lower = [&](const Task& t) -> int64_t {
     const GemvShape g = gemv_shape(m, t);

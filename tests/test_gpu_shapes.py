@@ -52,3 +52,24 @@ def test_attention_group_shapes(hd, nq, nkv):
     del eng
     agree, rel, mab = check_run(res, min_argmax=1.0)
     log(f"{wl.name}: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+# (weight format, bf16 projection inputs)
+QUANT = [("int8", False), ("int8", True), ("int4", False), ("int4", True)]
+
+
+@pytest.mark.parametrize("wfmt,act_bf16", QUANT, ids=lambda v: str(v))
+def test_tiny_quantised_formats(wfmt, act_bf16):
+    """The int8 and int4 GEMV bodies on a two-layer decoder (hidden 256, FFN
+    768 so that every int4 row holds whole groups of 128, random gains): 24-token
+    prompt + 16 decode steps, every step compared with the oracle, which
+    dequantises the same packed codes.  With bf16 projection inputs the int4
+    body's remainder terms are zero, so both of its input paths are taken."""
+    wl = synth.get("tiny").with_(name=f"tiny_{wfmt}_{'a16' if act_bf16 else 'a32'}", wfmt=wfmt,
+                                 act_bf16=act_bf16, ffn=768, prompt_len=24, decode_steps=16, max_ctx=64)
+    w = synth.model_weights(wl, seed=1, gains="random")
+    toks = synth.tokens(2, wl.prompt_len + wl.decode_steps, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks)
+    del eng
+    agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
+    log(f"{wl.name}: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")

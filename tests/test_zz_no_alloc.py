@@ -77,9 +77,13 @@ def test_noalloc_matches_allocated_engine_twice():
     assert ei.value.status == amk.ERR_UNSUPPORTED
     # a model whose engine state exceeds the scratch is refused before
     # anything is written: the live engine keeps decoding correctly
+    # (the 8192-position int4 model with 64 attention splits per kv head: its
+    # tagged attention partials alone are 68 MB)
     huge = synth.get("8b_int4")
     m = amk.ModelConfig.from_workload(huge)
-    sched = amk.Schedule.build(m, amk.default_schedule_config(m, device_cus()))
+    cfg = amk.default_schedule_config(m, device_cus())
+    cfg.attn_splits = 64
+    sched = amk.Schedule.build(m, cfg)
     dummy = [torch.zeros(256, dtype=torch.uint8, device="cuda") for _ in range(amk.packed_count(m))]
     kv = torch.zeros(256, dtype=torch.int16, device="cuda")
     logits = torch.zeros(16, dtype=torch.float32, device="cuda")
