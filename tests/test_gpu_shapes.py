@@ -73,3 +73,21 @@ def test_tiny_quantised_formats(wfmt, act_bf16):
     del eng
     agree, rel, mab = check_run(res, min_argmax=1.0, wl=wl)
     log(f"{wl.name}: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+@pytest.mark.parametrize("hd,nq,nkv", SHAPES, ids=lambda v: str(v))
+def test_attention_group_shapes_long_splits(hd, nq, nkv):
+    """The position-major attention layout (splits of 128 positions or more)
+    on every group shape: a two-layer decoder with a 384-position cache and
+    2 attention splits per kv head, 290-token prompt + 6 decode steps (splits
+    of 145..148 positions), every decode step compared with the oracle; the
+    prompt's steps take the head-major layout and build the cache on both
+    sides."""
+    wl = synth.get("tiny").with_(name=f"attnL_{hd}_{nq}_{nkv}", n_heads=nq, n_kv_heads=nkv,
+                                 head_dim=hd, prompt_len=290, decode_steps=6, max_ctx=384)
+    w = synth.model_weights(wl, seed=1, gains="random")
+    toks = synth.tokens(2, wl.prompt_len + wl.decode_steps, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks, compare_from=255, sched={"attn_splits": 2})
+    del eng
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"{wl.name}: {len(res)} steps compared, argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
