@@ -1570,7 +1570,8 @@ __device__ __forceinline__ bool attn_split_pm(const VmParams& P, TaskRef t, int 
     if (block_any(sp.failed, smem)) return false;
     trace_mark(P, t, 1);
   } else {
-    for (int i = tid; i < nq_w; i += kThreads) qs[i] = P.q[qbase + i] * scale;
+    const int nr = input_threads(P);
+    for (int i = tid; tid < nr && i < nq_w; i += nr) qs[i] = P.q[qbase + i] * scale;
     __syncthreads();
   }
   float q[GP][8];

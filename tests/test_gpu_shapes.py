@@ -91,3 +91,20 @@ def test_attention_group_shapes_long_splits(hd, nq, nkv):
     del eng
     agree, rel, mab = check_run(res, min_argmax=1.0)
     log(f"{wl.name}: {len(res)} steps compared, argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
+
+
+@pytest.mark.parametrize("sched", [{"sync_mode": 0}, {"poll_mode": 3}, {"poll_mode": 3, "sync_mode": 0},
+                                   {"sync_mode": 2}], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_attention_long_splits_under_schedule_knobs(sched):
+    """The position-major attention layout under the counter protocol (q and
+    the row at pos read after the acquire) and with DMA waves (positions on
+    waves 0..5, input reads by the input threads only): hd 128, 8 query heads
+    per kv head (two passes), 2 splits of 145+ positions."""
+    wl = synth.get("tiny").with_(name="attnL_knobs", n_heads=16, n_kv_heads=2, head_dim=128,
+                                 prompt_len=290, decode_steps=6, max_ctx=384)
+    w = synth.model_weights(wl, seed=1, gains="random")
+    toks = synth.tokens(2, wl.prompt_len + wl.decode_steps, wl.vocab)
+    res, eng, _ = teacher_forced(wl, w, toks, compare_from=255, sched=dict(sched, attn_splits=2))
+    del eng
+    agree, rel, mab = check_run(res, min_argmax=1.0)
+    log(f"{wl.name} {sched}: {len(res)} steps, argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
