@@ -12,7 +12,13 @@ byte (projections, scales, norms, LM head) + one embedding row + the KV
 bytes of positions 0..p + the fp32 logits.  The `roofline` object gives the
 achieved algorithmic GB/s of the single kernel (amk_vm) per launch, timed
 with HIP events on the launch stream.  `cpu_baseline` times the oracle on a
-bounded sample of the same workload on this host's cores.
+bounded sample of the same workload on this host's cores.  Also on the line:
+`stream_read` (a plain streaming read of the largest weight tensor on the
+same device, the measured bandwidth ceiling), `launch_overhead_us` (the same
+cooperative kernel launched with every queue empty), `counter_protocol` (the
+same positions with the pages' counter protocol instead of the default
+tagged activations) and, with --multistep, `multistep` (the same positions
+as one greedy multi-step launch).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b]
 
@@ -362,6 +368,19 @@ def main():
         rates.append(big.numel() * big.element_size() * 5 / (e0.elapsed_time(e1) * 1e-3))
     out["stream_read"] = {"GBps": max(rates) / 1e9, "bytes": int(big.numel() * big.element_size()),
                           "kernel_frac": achieved / max(rates)}
+    # the cooperative-launch overhead of a step: the same kernel, grid, LDS
+    # and parameters with every queue empty (amk_engine_launch_empty),
+    # back to back on the launch stream
+    for _ in range(4):
+        eng.launch_empty(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(64):
+        eng.launch_empty(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eng.check()
+    out["launch_overhead_us"] = e0.elapsed_time(e1) * 1e3 / 64
     if not args.no_counter_protocol and cfg.sync_mode != 0:
         # the same positions with the pages' counter protocol (sync_mode 0):
         # same DAG, every edge a monotonic counter (wait -> dispatch ->

@@ -428,6 +428,17 @@ amk_status amk_engine_set_kv_length(amk_engine* engine, int32_t n_positions);
  * are undefined), AMK_OK otherwise. */
 amk_status amk_engine_check(amk_engine* engine);
 
+/* The cooperative-launch overhead of a decode step (the measurement the
+ * scope table's evidence list asks for; the AMK summary, "Methodology",
+ * layer 0, puts the whole forward pass in one launch so that this cost is
+ * paid once per token): enqueue one launch of the engine's decode kernel
+ * with the same grid, block, LDS and parameters as amk_decode_step, but
+ * with every queue empty, so no task runs and nothing is read or written
+ * beyond the kernel's own queue offsets.  Asynchronous on hip_stream; the
+ * engine's state (positions, counters, tags) is unchanged.  AMK_ERR_INVALID_ARG
+ * for a null engine or one whose static scratch was taken over. */
+amk_status amk_engine_launch_empty(amk_engine* engine, void* hip_stream);
+
 /* Per-launch spin budget in microseconds for device-side waits (default
  * 2,000,000).  Every wait of a launch gives up once the budget is spent and
  * the launch then drains; amk_engine_check reports it. */

@@ -133,6 +133,7 @@ _SIGS = {
     "amk_decode_step": ([_p, _i32, _i32, _p], _i32),
     "amk_decode_steps": ([_p, _i32, _i32, _i32, _p, _p], _i32),
     "amk_engine_check": ([_p], _i32),
+    "amk_engine_launch_empty": ([_p, _p], _i32),
     "amk_engine_set_spin_budget": ([_p, _i64], _i32),
     "amk_engine_set_kv_length": ([_p, _i32], _i32),
     "amk_engine_set_trace": ([_p, _i32], _i32),
@@ -426,6 +427,13 @@ class Engine:
 
     def check(self):
         _check(_lib.amk_engine_check(self._h), "amk_engine_check")
+
+    def launch_empty(self, stream=None):
+        """One launch of the decode kernel with every queue empty (the
+        cooperative-launch overhead of a step); nothing runs or changes."""
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        _check(_lib.amk_engine_launch_empty(self._h, ctypes.c_void_p(s.cuda_stream)), "amk_engine_launch_empty")
 
     def set_kv_length(self, n):
         _check(_lib.amk_engine_set_kv_length(self._h, int(n)), "amk_engine_set_kv_length")

@@ -149,6 +149,9 @@ struct amk_engine {
   std::vector<size_t> tag_words;
   // the schedule passes amk_multistep_check (amk_decode_steps allowed)
   bool multistep_ok = false;
+  // num_cus + 1 zeros: queue offsets of a launch in which every queue is
+  // empty (amk_engine_launch_empty)
+  int32_t* qoff_empty = nullptr;
   // amk_engine_create_noalloc: every device region of the engine is carved
   // from this device's static scratch array (nothing allocated, nothing
   // freed); null for engines whose regions were allocated
@@ -574,7 +577,7 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
 
   VmParams& pr = e->params;
   DevTask* d_tasks = nullptr;
-  int32_t *d_qoff = nullptr, *d_queue = nullptr;
+  int32_t *d_qoff = nullptr, *d_queue = nullptr, *d_qoff_empty = nullptr;
   const uint8_t** d_wptr = nullptr;
   float2* d_rope = nullptr;
   const int64_t L = m.n_layers, S = c.attn_splits, H = m.hidden, F = m.ffn;
@@ -585,9 +588,11 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
   pr.n_steps = 1;
   pr.n_lm = n_lm;
   pr.tokens_out = nullptr;
+  const std::vector<int32_t> qoff_empty((size_t)c.num_cus + 1, 0);
   std::vector<Region> regions;
   add_region(&regions, &d_tasks, dt);
   add_region(&regions, &d_qoff, qoff);
+  add_region(&regions, &d_qoff_empty, qoff_empty);
   add_region(&regions, &d_queue, queue);
   add_region(&regions, &d_wptr, wptr);
   add_region(&regions, &d_rope, rope);
@@ -627,6 +632,7 @@ amk_status create_engine(const amk_schedule* s, const amk_device_buffers* bufs, 
   }
   pr.tasks = d_tasks;
   pr.queue_off = d_qoff;
+  e->qoff_empty = d_qoff_empty;
   pr.queue = d_queue;
   pr.wptr = d_wptr;
   pr.rope = d_rope;
@@ -682,6 +688,20 @@ amk_status amk_decode_steps(amk_engine* e, int32_t token, int32_t pos, int32_t n
     return fail(AMK_ERR_UNSUPPORTED, "the engine's schedule fails amk_multistep_check: a multi-step launch could "
                                      "start a step while a task of the previous one still runs");
   return amk::launch_steps(e, token, pos, n_steps, tokens_out, stream);
+}
+
+amk_status amk_engine_launch_empty(amk_engine* e, void* stream) {
+  if (!e) return fail(AMK_ERR_INVALID_ARG, "null engine");
+  amk_status live = check_live(e);
+  if (live != AMK_OK) return live;
+  amk::VmParams p = e->params;
+  p.queue_off = e->qoff_empty;
+  p.n_steps = 1;
+  p.tokens_out = nullptr;
+  void* args[] = {&p};
+  HIP_TRY(hipLaunchCooperativeKernel(e->kernel, dim3(e->config.num_cus), dim3(kThreads), args, (unsigned)e->lds_bytes,
+                                     static_cast<hipStream_t>(stream)));
+  return AMK_OK;
 }
 
 amk_status amk_engine_check(amk_engine* e) {

@@ -11,7 +11,7 @@ import pytest
 import oracle
 import persistent_megakernel_wg_amd as amk
 import synth
-from tests.gpu_common import compare, gpu_step, log, make_engine
+from tests.gpu_common import MAX_ABS, REL_L2, compare, gpu_step, log, make_engine
 from tests.validator_common import lowered
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +173,32 @@ def test_engine_refuses_unexecutable_nops_and_unsafe_multistep(tiny):
     sch.close()
     orc.close()
     log("engine: late QKV copy decodes single steps, refuses multi-step; NOP with accesses refused")
+
+
+def test_empty_launch_changes_nothing():
+    """amk_engine_launch_empty runs the decode kernel with every queue empty:
+    the logits of the previous step stay bit-identical, and the next steps
+    still match the oracle (no position, counter or tag moved)."""
+    import torch
+    wl = synth.get("tiny")
+    w = synth.model_weights(wl, seed=1, gains="random")
+    toks = synth.tokens(2, 12, wl.vocab)
+    eng = make_engine(wl, w)
+    orc = oracle.Model(wl, w)
+    kv_o = orc.new_kv()
+    for pos in range(6):
+        g = gpu_step(eng, int(toks[pos]), pos)
+        orc.step(kv_o, int(toks[pos]), pos)
+    before = eng.logits.clone()
+    for _ in range(3):
+        eng.launch_empty()
+    torch.cuda.synchronize()
+    eng.check()
+    assert torch.equal(before, eng.logits)
+    for pos in range(6, 12):
+        g = gpu_step(eng, int(toks[pos]), pos)
+        o = orc.step(kv_o, int(toks[pos]), pos)
+        rel, mab, ok = compare(g, o)
+        assert rel <= REL_L2 and mab <= MAX_ABS and ok, (pos, rel, mab)
+    orc.close()
+    eng.close()
