@@ -23,6 +23,8 @@ as one greedy multi-step launch).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b]
 
 Helpers for the committed profiles (see the command line in each summary):
+  --no-launch-overhead    skip the empty-queue launches (under a profiler they
+                          would be dispatches of the same kernel)
   --prompt-kv synthetic   fill the prompt's KV rows with seeded values instead
                           of running the prompt through the kernel (decode
                           time does not depend on KV values); used under the
@@ -116,8 +118,13 @@ def traffic_from(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv)
     copy_pat = "copyBuffer"  # the runtime's device-to-device copy kernel behind torch's copy_
     cf, ncf = med(_counter_rows(copy_fetch_csv, "FETCH_SIZE"), copy_pat)
     cw, ncw = med(_counter_rows(copy_write_csv, "WRITE_SIZE"), copy_pat)
-    kf, nkf = med(_counter_rows(fetch_csv, "FETCH_SIZE"), "amk_vm")
-    kw, nkw = med(_counter_rows(write_csv, "WRITE_SIZE"), "amk_vm")
+    # decode-step dispatches only: an empty-queue launch of the same kernel
+    # (the launch-overhead measurement) reads next to nothing
+    def steps_only(rows):
+        big = max(v for k, v in rows if "amk_vm" in k)
+        return [(k, v) for k, v in rows if v >= 0.01 * big]
+    kf, nkf = med(steps_only(_counter_rows(fetch_csv, "FETCH_SIZE")), "amk_vm")
+    kw, nkw = med(steps_only(_counter_rows(write_csv, "WRITE_SIZE")), "amk_vm")
     fscale = COPY_BYTES / (cf * 1024.0)
     wscale = COPY_BYTES / (cw * 1024.0)
     out = {"workload": workload, "kernel_sha256_16": kernel_hash(),
@@ -224,6 +231,8 @@ def main():
     ap.add_argument("--probe", choices=("", "copy"), default="")
     ap.add_argument("--no-counter-protocol", action="store_true",
                     help="skip timing the same positions with the counter protocol (sync_mode 0)")
+    ap.add_argument("--no-launch-overhead", action="store_true",
+                    help="skip the empty-queue launches (profiler runs: they are dispatches of the same kernel)")
     ap.add_argument("--multistep", action="store_true",
                     help="also time the same positions as one greedy multi-step launch")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -371,16 +380,17 @@ def main():
     # the cooperative-launch overhead of a step: the same kernel, grid, LDS
     # and parameters with every queue empty (amk_engine_launch_empty),
     # back to back on the launch stream
-    for _ in range(4):
-        eng.launch_empty(stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(64):
-        eng.launch_empty(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eng.check()
-    out["launch_overhead_us"] = e0.elapsed_time(e1) * 1e3 / 64
+    if not args.no_launch_overhead:
+        for _ in range(4):
+            eng.launch_empty(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(64):
+            eng.launch_empty(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eng.check()
+        out["launch_overhead_us"] = e0.elapsed_time(e1) * 1e3 / 64
     if not args.no_counter_protocol and cfg.sync_mode != 0:
         # the same positions with the pages' counter protocol (sync_mode 0):
         # same DAG, every edge a monotonic counter (wait -> dispatch ->
