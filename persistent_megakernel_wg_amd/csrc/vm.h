@@ -468,37 +468,33 @@ __device__ __forceinline__ void vm_signal(const VmParams& P, TaskRef t) {
 //   rounds: while 8 whole units remain, wave w owns unit w of the round, so
 //           the 8 waves stream 8 adjacent rows side by side (the workgroup's
 //           reads stay within a few DRAM pages);
-//   tail:   the R = nunits % 8 last units are cut into p = 8 / R (at most J)
-//           equal slab ranges each; wave w < R*p takes piece w % p of tail
-//           unit w / p.
-// So a wave's steps form its round units plus at most one tail segment, and
-// every segment lies inside one unit.  Each wave writes one partial per
-// segment to an LDS table; the finalize pass adds, per row, the partials of
-// the waves that covered its unit, in wave order (bit-reproducible).  Each
+//   tail:   the R = nunits % 8 last units hold R*J steps; wave w takes the
+//           contiguous steps [w*R*J/8, (w+1)*R*J/8) of them in unit-major
+//           order, so every wave's share differs by at most one step (a
+//           task's time then follows its row count in fine steps, which
+//           lets the per-XCD row shares move work between queues).
+// So a wave's steps form its round units plus at most one tail range, which
+// spans at most two units (a range is shorter than J steps).  Each wave writes
+// one partial per unit segment to an LDS table; the finalize pass adds, per
+// row, the partials of the waves that covered its unit, in wave order
+// (bit-reproducible).  Each
 // wave keeps DS steps of loads in flight in a register ring; the first DS are
 // issued before the task's wait (for wave 0, which polls, after it when
 // poll_late is set: a poll then does not queue behind its own weight loads).
 // Buffer loads whose offset lies past the task's rows return zero without
 // memory traffic.
 struct GemvSplit {
-  int J, nr, R, p, pl;  // slabs per row, rounds, tail units, pieces per tail unit, piece length
+  int J, nr, R, TS;  // slabs per row, rounds, tail units, tail steps
   __device__ __forceinline__ GemvSplit(int nunits, int J_) : J(J_) {
     nr = nunits / kWaves;
     R = nunits - nr * kWaves;
-    p = R == 0 ? 0 : min(kWaves / R, J);
-    pl = p == 0 ? 0 : (J + p - 1) / p;
+    TS = R * J;
   }
-  // tail segment of wave w: unit (index), first slab, length (0: none)
-  __device__ __forceinline__ void tail(int w, int* unit, int* j0, int* len) const {
-    *unit = 0;
-    *j0 = 0;
-    *len = 0;
-    if (w < R * p) {
-      const int q = w / p, k = w - q * p;
-      *unit = nr * kWaves + q;
-      *j0 = k * pl;
-      *len = max(0, min(J, *j0 + pl) - *j0);
-    }
+  // tail steps [t0, t1) of wave w; tail step t is slab t % J of unit
+  // nr * kWaves + t / J
+  __device__ __forceinline__ void tail(int w, int* t0, int* t1) const {
+    *t0 = (TS * w) / kWaves;
+    *t1 = (TS * (w + 1)) / kWaves;
   }
 };
 
@@ -785,19 +781,22 @@ struct StepIter {
   __device__ __forceinline__ void init(int sw, int nunits, int J_) {
     J = J_;
     const GemvSplit sp(nunits, J);
-    int t_len;
-    sp.tail(sw, &t_unit, &t_j0, &t_len);
+    int t0, t1;
+    sp.tail(sw, &t0, &t1);
+    t_unit = sp.nr * kWaves + t0 / J;
+    t_j0 = t0 % J;
     nA = sp.nr * J;
-    n = nA + t_len;
+    n = nA + (t1 - t0);
     ik = 0;
     iu = nA ? sw : t_unit;
     ij = nA ? 0 : t_j0;
   }
+  // rounds: the next slab, then unit + 8; tail: the next slab, then the next unit
   __device__ __forceinline__ void advance() {
     ++ik;
     if (++ij == J) {
       ij = 0;
-      iu += kWaves;
+      iu += ik <= nA ? kWaves : 1;
     }
     if (ik == nA) {
       iu = t_unit;
@@ -943,16 +942,20 @@ __device__ __forceinline__ void gemv(const uint8_t* data, const uint8_t* meta, u
 }
 
 // sum of the partials of output row i (unit u = i / RPU): its owner in the
-// rounds, or the waves whose tail piece lies in unit u, in wave order
+// rounds, or the waves whose tail range overlaps unit u, in wave order
 template <int RPU>
 __device__ __forceinline__ float gemv_row(const float* tbl, int i, int nunits, int J) {
   const int u = i / RPU;
   const GemvSplit sp(nunits, J);
   if (u < sp.nr * kWaves) return tbl[i * kWaves + u % kWaves];
-  const int q = u - sp.nr * kWaves;
+  const int q0 = (u - sp.nr * kWaves) * J, q1 = q0 + J;  // the unit's tail steps
   float v = 0.0f;
-  for (int k = 0; k < sp.p; ++k)
-    if (k * sp.pl < J) v += tbl[i * kWaves + q * sp.p + k];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    int t0, t1;
+    sp.tail(w, &t0, &t1);
+    if (t1 > t0 && t0 < q1 && t1 > q0) v += tbl[i * kWaves + w];  // (empty ranges wrote nothing)
+  }
   return v;
 }
 
