@@ -202,3 +202,38 @@ def test_empty_launch_changes_nothing():
         assert rel <= REL_L2 and mab <= MAX_ABS and ok, (pos, rel, mab)
     orc.close()
     eng.close()
+
+
+def test_last_position_and_rewind_long_splits():
+    """The position-major attention layout at the cache's end: a two-layer
+    decoder with a 300-position cache and 2 splits per kv head decodes up to
+    position 299 (splits of 150 positions, the last block of each ragged),
+    then rewinds to position 262 and decodes a different continuation; every
+    step from position 255 on matches the oracle."""
+    wl = synth.get("tiny").with_(name="tiny_end_long", max_ctx=300, prompt_len=256, decode_steps=44)
+    w = synth.model_weights(wl, seed=1, gains="random")
+    n = wl.max_ctx
+    toks = synth.tokens(4, n, wl.vocab)
+    alt = synth.tokens(5, 8, wl.vocab)
+    eng = make_engine(wl, w, {"attn_splits": 2})
+    orc = oracle.Model(wl, w)
+    kv_o = orc.new_kv()
+    worst = 0.0
+    for p in range(n):
+        g = gpu_step(eng, int(toks[p]), p)
+        o = orc.step(kv_o, int(toks[p]), p)
+        if p >= 255:
+            rel, mab, same = compare(g, o)
+            worst = max(worst, rel)
+            assert rel <= REL_L2 and mab <= MAX_ABS and same, (p, rel, mab)
+    r = 262
+    kv_o[:, :, :, r:, :] = 0
+    for i, tok in enumerate(alt):
+        g = gpu_step(eng, int(tok), r + i)
+        o = orc.step(kv_o, int(tok), r + i)
+        rel, mab, same = compare(g, o)
+        worst = max(worst, rel)
+        assert rel <= REL_L2 and mab <= MAX_ABS and same, (r + i, rel, mab)
+    log(f"tiny, 300-position cache, 2 splits: to pos {n - 1} and rewound to {r}: worst relL2 {worst:.2e}")
+    orc.close()
+    eng.close()
