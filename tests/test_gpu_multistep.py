@@ -55,15 +55,25 @@ def _oracle_greedy(wl, w, prompt, p0, n, kv_prefix=None):
     return toks, o
 
 
-@pytest.mark.parametrize("sync_mode", [1, 0])
-def test_multistep_matches_host_loop_and_oracle(sync_mode):
+@pytest.mark.parametrize("sync_mode,long_splits", [(1, False), (0, False), (1, True)],
+                         ids=["tagged", "counters", "tagged-long-splits"])
+def test_multistep_matches_host_loop_and_oracle(sync_mode, long_splits):
+    """long_splits: a 300-position cache, 2 attention splits per kv head and
+    a 257-token prompt, so every greedy step (positions 256..275) takes the
+    position-major attention layout (splits of 128+ positions)."""
     import torch
     wl = synth.get("tiny")
+    sched = {"sync_mode": sync_mode}
+    plen = 8
+    if long_splits:
+        wl = wl.with_(name="tiny_ms_long", max_ctx=300, prompt_len=256, decode_steps=40)
+        sched["attn_splits"] = 2
+        plen = 257
     w = synth.model_weights(wl, seed=1)
-    prompt = synth.tokens(2, 8, wl.vocab)
+    prompt = synth.tokens(2, plen, wl.vocab)
     n = 20
-    a, sa = _engine(wl, w, sync_mode=sync_mode)
-    b, sb = _engine(wl, w, sync_mode=sync_mode)
+    a, sa = _engine(wl, w, **sched)
+    b, sb = _engine(wl, w, **sched)
     for i, t in enumerate(prompt[:-1]):
         a.decode_step(int(t), i)
         b.decode_step(int(t), i)
@@ -81,7 +91,7 @@ def test_multistep_matches_host_loop_and_oracle(sync_mode):
     assert orc_toks == dev_toks, (orc_toks, dev_toks)
     rel, mab, same = compare(host_logits.astype(np.float64), o, bars(wl)[2])
     assert rel <= bars(wl)[0] and mab <= bars(wl)[1] and same, (rel, mab)
-    log(f"multistep sync_mode {sync_mode}: {n} tokens identical to the host loop and the oracle, "
+    log(f"multistep {wl.name} sync_mode {sync_mode}: {n} tokens identical to the host loop and the oracle, "
         f"final relL2 {rel:.2e}")
     for e, s in ((a, sa), (b, sb)):
         e.close()
