@@ -262,8 +262,9 @@ def test_sync_mode_limits():
 def test_defaults_follow_format_and_context():
     """Automatic schedule fields: 64 KB prefetch for bf16 weights, none for
     int8 / int4 and smaller models; 3/4 of the queues run attention splits
-    (8 per kv head up to a 512-position cache)."""
-    for name, splits, pf in (("8b", 24, 64), ("8b_int8", 24, -1), ("8b_int4", 24, -1), ("1b", 8, -1), ("tiny", 8, -1)):
+    (8 per kv head up to a 512-position cache; past 4096 positions, as many
+    as leave one split-free queue per query head)."""
+    for name, splits, pf in (("8b", 24, 64), ("8b_int8", 24, -1), ("8b_int4", 28, -1), ("1b", 8, -1), ("tiny", 8, -1)):
         m = amk.ModelConfig.from_workload(synth.get(name))
         d = amk.default_schedule_config(m, 256).as_dict()
         assert (d["attn_splits"], d["prefetch_kb"]) == (splits, pf), name
