@@ -85,9 +85,11 @@ typedef struct {
   int32_t tiles_qkv, tiles_o, tiles_gateup, tiles_down, tiles_lm;
   int32_t attn_splits;     /* position splits per kv head (log-sum-exp merged);
                             * automatic: 3/4 of num_cus / n_kv_heads, so that
-                            * a quarter of the queues run no attention split
-                            * (all of num_cus / n_kv_heads when max_ctx > 4096,
-                            * 8 when max_ctx <= 512) */
+                            * a quarter of the queues run no attention split;
+                            * (num_cus - n_heads) / n_kv_heads when max_ctx >
+                            * 4096 (one split-free queue per query head, for
+                            * its merge); min(8, num_cus / n_kv_heads) when
+                            * max_ctx <= 512 */
   int32_t cu_policy;       /* 0: task i of T -> queue i*num_cus/T; 1: i % num_cus */
   int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16 */
   uint32_t fuse_flags;     /* AMK_FUSE_* bits; only AMK_FUSE_DEFAULT is built */
