@@ -268,3 +268,29 @@ def test_defaults_follow_format_and_context():
         m = amk.ModelConfig.from_workload(synth.get(name))
         d = amk.default_schedule_config(m, 256).as_dict()
         assert (d["attn_splits"], d["prefetch_kb"]) == (splits, pf), name
+
+
+@pytest.mark.parametrize("ncu,nq,nkv", [(256, 32, 8), (304, 64, 8), (80, 32, 8), (64, 16, 4), (40, 32, 8),
+                                        (24, 32, 8), (16, 4, 2), (8, 4, 2)])
+def test_long_context_default_splits_leave_a_queue_per_merge(ncu, nq, nkv):
+    """Past 4096 positions the automatic split count is
+    max(1, (num_cus - n_heads) / n_kv_heads): the lowering passes the gate,
+    no merge shares a queue with an attention split of its layer, and every
+    merge has a queue of its own whenever the queues suffice."""
+    wl = synth.get("tiny").with_(n_heads=nq, n_kv_heads=nkv, hidden=nq * 64, max_ctx=8192)
+    m = amk.ModelConfig.from_workload(wl)
+    cfg = amk.default_schedule_config(m, ncu)
+    assert cfg.attn_splits == max(1, (ncu - nq) // nkv)
+    s = amk.Schedule.build(m, cfg)
+    try:
+        assert s.validate()[0] == 0
+        v = s.view()
+        for layer in range(wl.n_layers):
+            attn_q = {t["cu"] for t in v["tasks"] if t["type"] == 2 and t["p"][0] == layer}
+            merge_q = [t["cu"] for t in v["tasks"] if t["type"] == 3 and t["p"][0] == layer]
+            assert len(attn_q) == cfg.attn_splits * nkv
+            assert not attn_q & set(merge_q)
+            if ncu - cfg.attn_splits * nkv >= nq:
+                assert len(set(merge_q)) == len(merge_q) == nq
+    finally:
+        s.close()
