@@ -370,7 +370,7 @@ amk_status amk_engine_create(const amk_schedule* schedule, const amk_device_buff
                              amk_engine** out);
 
 /* Bytes of the static device scratch behind amk_engine_create_noalloc. */
-#define AMK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+#define AMK_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
 
 /* amk_engine_create without any device allocation, for callers that cannot
  * allocate device memory: code that runs under HIP graph capture, serving

@@ -28,7 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNSAFE_SCHEDULE, ERR_OUT_OF_RANGE, ERR_HIP, \
     ERR_NOMEM, ERR_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
-NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # AMK_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # AMK_NOALLOC_SCRATCH_BYTES
 W_BF16, W_INT8_ROW, W_INT4_G128 = 0, 1, 2
 WFMT = {"bf16": W_BF16, "int8": W_INT8_ROW, "int4": W_INT4_G128}
 TASK_NOP, TASK_QKV, TASK_ATTN, TASK_MERGE, TASK_OPROJ, TASK_GATEUP, TASK_DOWN, TASK_LMHEAD = range(8)

@@ -77,8 +77,8 @@ def test_noalloc_matches_allocated_engine_twice():
     assert ei.value.status == amk.ERR_UNSUPPORTED
     # a model whose engine state exceeds the scratch is refused before
     # anything is written: the live engine keeps decoding correctly
-    # (the 8192-position int4 model with 64 attention splits per kv head: its
-    # tagged attention partials alone are 68 MB)
+    # (the 8192-position int4 model with 64 attention splits per kv head:
+    # its engine state is about 126 MB, beyond the 96 MiB scratch)
     huge = synth.get("8b_int4")
     m = amk.ModelConfig.from_workload(huge)
     cfg = amk.default_schedule_config(m, device_cus())
@@ -104,4 +104,13 @@ def test_noalloc_matches_allocated_engine_twice():
     assert rel <= REL_L2 and mab <= MAX_ABS and ok
     orc.close()
     second.close()
-    log("noalloc: takeover refused the earlier engine, oversize refused, live engine intact")
+    # the largest engine state among the workloads here, the int4 model's
+    # with its default 28 splits per kv head, fits: created (and destroyed)
+    # without a launch
+    cfg = amk.default_schedule_config(m, device_cus())
+    sched = amk.Schedule.build(m, cfg)
+    fits = amk.Engine(sched, dummy, kv, logits, noalloc=True)
+    fits.close()
+    sched.close()
+    log("noalloc: takeover refused the earlier engine, oversize refused, live engine intact, "
+        "the default int4 engine fits")
