@@ -91,7 +91,9 @@ typedef struct {
                             * its merge); min(8, num_cus / n_kv_heads) when
                             * max_ctx <= 512 */
   int32_t cu_policy;       /* 0: task i of T -> queue i*num_cus/T; 1: i % num_cus */
-  int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16 */
+  int32_t pipeline_depth;  /* 16-byte weight loads in flight per lane: 4, 8, 16
+                            * (amk_default_schedule_config: 4 for int4
+                            * weights, 8 otherwise) */
   uint32_t fuse_flags;     /* AMK_FUSE_* bits; only AMK_FUSE_DEFAULT is built */
   /* Queue-walk knobs (no effect on the DAG the safety gate checks):
    * poll_mode 0: the polling wave issues its weight prologue before the
@@ -99,6 +101,8 @@ typedef struct {
    *   behind its own loads); 2: every wave issues half of its ring before
    *   the wait and half once the wait is over, so that loads issued after
    *   the input arrived keep HBM busy while the input is staged.
+   *   amk_default_schedule_config: 2 where the LDS prefetch runs (bf16
+   *   weights, hidden >= 4096), 1 otherwise.
    * prefetch_kb: LDS kilobytes per task into which the end of the previous
    *   task of the queue copies the task's first weight slabs (LDS DMA), so
    *   streaming goes on through waits; 0 = 64 KB for bf16 weights with

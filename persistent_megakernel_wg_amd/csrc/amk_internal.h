@@ -103,6 +103,8 @@ namespace amk {
 amk_status check_model(const amk_model_config& m);
 amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& in,
                           amk_schedule_config* out);
+// the automatic attention split count (ScheduleConfig attn_splits = 0)
+int32_t default_attn_splits(const amk_model_config& m, int32_t num_cus);
 
 // standard buffer table of a lowered model
 std::vector<Buffer> buffer_table(const amk_model_config& m, int32_t attn_splits);

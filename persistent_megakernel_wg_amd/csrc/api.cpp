@@ -51,15 +51,22 @@ amk_status amk_default_schedule_config(const amk_model_config* model, int32_t de
   c.num_cus = device_cus;
   c.wg_threads = 512;
   c.cu_policy = 0;
-  c.pipeline_depth = 8;
+  // the schedule tuner's picks on the final kernel, gated on the oracle's
+  // logits: a 4-deep ring for int4 weights (a 16-byte load holds 32 of them;
+  // 8b_int4 2.464 -> 2.427 ms) and 8 otherwise; the polling wave issues its
+  // ring loads before the wait only where the LDS prefetch runs (bf16 at
+  // hidden >= 4096: half of the ring after the wait, so that loads issued
+  // once the input has arrived keep HBM busy while it is staged), and after
+  // the wait elsewhere, so that its input read queues behind none of them
+  // (1b 0.872 -> 0.854 ms, 8b_int8 2.353 -> 2.337, 8b_int4 at depth 4
+  // 2.427 -> 2.410; the 8B bf16 step is the same in both modes)
+  c.pipeline_depth = model->wfmt == AMK_W_INT4_G128 ? 4 : 8;
   c.fuse_flags = AMK_FUSE_DEFAULT;
   // tagged activations where the split count allows them (they measured
   // faster than the counter protocol on the 8B shape)
   c.sync_mode = 1;
-  c.poll_mode = 2;  // half of the ring after the wait (measured faster on the 8B shape)
-  const int32_t splits = model->max_ctx <= 512
-                             ? std::min(8, std::max(1, device_cus / model->n_kv_heads))
-                             : std::max(1, (model->max_ctx > 4096 ? 4 : 3) * device_cus / (4 * model->n_kv_heads));
+  c.poll_mode = model->wfmt == AMK_W_BF16 && model->hidden >= 4096 ? 2 : 1;
+  const int32_t splits = default_attn_splits(*model, device_cus);
   if (splits > 512 || (int64_t)splits * model->head_dim > 8192) c.sync_mode = 0;
   return resolve_config(*model, c, out);
 }

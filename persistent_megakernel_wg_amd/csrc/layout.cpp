@@ -39,6 +39,19 @@ amk_status check_model(const amk_model_config& m) {
 
 static int32_t pick(int32_t v, int32_t dflt) { return v > 0 ? v : dflt; }
 
+// Automatic split count: 3/4 of the queues run a split (8 per kv head for
+// caches of at most 512 positions: short splits cost more in merging than
+// they save).  Caches of more than 4096 positions take as many splits as
+// leave one split-free queue per query head, where the merges go (on the
+// 8192-position int4 workload, 28 splits per kv head: 2.457 ms; 24: 2.485;
+// 30, two merges on some queues: 2.638; the position-major attention layout
+// keeps such long splits fast).
+int32_t default_attn_splits(const amk_model_config& m, int32_t num_cus) {
+  if (m.max_ctx <= 512) return std::min(8, std::max(1, num_cus / m.n_kv_heads));
+  if (m.max_ctx <= 4096) return std::max(1, 3 * num_cus / (4 * m.n_kv_heads));
+  return std::max(1, (num_cus - m.n_heads) / m.n_kv_heads);
+}
+
 amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& in,
                           amk_schedule_config* out) {
   amk_schedule_config c = in;
@@ -58,17 +71,7 @@ amk_status resolve_config(const amk_model_config& m, const amk_schedule_config& 
   c.tiles_gateup = std::min(c.tiles_gateup, m.ffn);
   c.tiles_down = std::min(c.tiles_down, std::max(1, m.hidden / 2));
   c.tiles_lm = std::min(c.tiles_lm, std::max(1, m.vocab / 2));
-  // automatic split count: 3/4 of the queues run a split (8 per kv head for
-  // caches of at most 512 positions: short splits cost more in merging than
-  // they save).  Caches of more than 4096 positions take as many splits as
-  // leave one split-free queue per query head, where the merges go (on the
-  // 8192-position int4 workload, 28 splits per kv head: 2.457 ms; 24: 2.485;
-  // 30, two merges on some queues: 2.638; the position-major attention layout
-  // keeps such long splits fast).
-  if (c.attn_splits <= 0)
-    c.attn_splits = m.max_ctx <= 512  ? std::min(8, std::max(1, c.num_cus / m.n_kv_heads))
-                    : m.max_ctx <= 4096 ? std::max(1, 3 * c.num_cus / (4 * m.n_kv_heads))
-                                        : std::max(1, (c.num_cus - m.n_heads) / m.n_kv_heads);
+  if (c.attn_splits <= 0) c.attn_splits = default_attn_splits(m, c.num_cus);
   if (c.attn_splits > 256) return fail(AMK_ERR_UNSUPPORTED, "attn_splits must be at most 256");
   if (c.cu_policy != 0 && c.cu_policy != 1) return fail(AMK_ERR_UNSUPPORTED, "cu_policy must be 0 or 1");
   if (c.pipeline_depth == 0) c.pipeline_depth = 8;

@@ -260,14 +260,17 @@ def test_sync_mode_limits():
 
 
 def test_defaults_follow_format_and_context():
-    """Automatic schedule fields: 64 KB prefetch for bf16 weights, none for
-    int8 / int4 and smaller models; 3/4 of the queues run attention splits
-    (8 per kv head up to a 512-position cache; past 4096 positions, as many
-    as leave one split-free queue per query head)."""
-    for name, splits, pf in (("8b", 24, 64), ("8b_int8", 24, -1), ("8b_int4", 28, -1), ("1b", 8, -1), ("tiny", 8, -1)):
+    """Automatic schedule fields: 64 KB prefetch and half of the ring issued
+    after the wait for bf16 weights at hidden >= 4096, no prefetch and the
+    polling wave's ring after the wait otherwise; a 4-deep ring for int4
+    weights, 8 otherwise; 3/4 of the queues run attention splits (8 per kv
+    head up to a 512-position cache; past 4096 positions, as many as leave
+    one split-free queue per query head)."""
+    for name, splits, pf, poll, depth in (("8b", 24, 64, 2, 8), ("8b_int8", 24, -1, 1, 8), ("8b_int4", 28, -1, 1, 4),
+                                          ("1b", 8, -1, 1, 8), ("tiny", 8, -1, 1, 8)):
         m = amk.ModelConfig.from_workload(synth.get(name))
         d = amk.default_schedule_config(m, 256).as_dict()
-        assert (d["attn_splits"], d["prefetch_kb"]) == (splits, pf), name
+        assert (d["attn_splits"], d["prefetch_kb"], d["poll_mode"], d["pipeline_depth"]) == (splits, pf, poll, depth), name
 
 
 @pytest.mark.parametrize("ncu,nq,nkv", [(256, 32, 8), (304, 64, 8), (80, 32, 8), (64, 16, 4), (40, 32, 8),

@@ -112,7 +112,7 @@ def test_full_size_long_context(name, w8b):
     log(f"{name} long: argmax {agree:.3f} worst relL2 {rel:.2e} worst maxabs {mab:.2e}")
 
 
-@pytest.mark.parametrize("sched", [{"prefetch_kb": -1}, {"prefetch_kb": 4}, {"poll_mode": 1},
+@pytest.mark.parametrize("sched", [{"prefetch_kb": -1}, {"prefetch_kb": 4}, {"poll_mode": 1}, {"poll_mode": 2},
                                    {"poll_mode": 0}, {"poll_mode": 2, "pipeline_depth": 16},
                                    {"poll_mode": 2, "sync_mode": 0},
                                    {"sync_mode": 0}, {"sync_mode": 0, "poll_mode": 1},
