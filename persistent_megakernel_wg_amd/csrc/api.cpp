@@ -51,8 +51,8 @@ amk_status amk_default_schedule_config(const amk_model_config* model, int32_t de
   c.num_cus = device_cus;
   c.wg_threads = 512;
   c.cu_policy = 0;
-  // the schedule tuner's picks on the final kernel, gated on the oracle's
-  // logits: a 4-deep ring for int4 weights (a 16-byte load holds 32 of them;
+  // the schedule tuner's picks (its runs gated on the oracle's reference
+  // logits): a 4-deep ring for int4 weights (a 16-byte load holds 32 of them;
   // 8b_int4 2.464 -> 2.427 ms) and 8 otherwise; the polling wave issues its
   // ring loads before the wait only where the LDS prefetch runs (bf16 at
   // hidden >= 4096: half of the ring after the wait, so that loads issued
