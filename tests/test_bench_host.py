@@ -4,7 +4,9 @@ roofline, checked against the byte count of each stored tensor written out
 from the model shapes and the weight formats' definitions (bf16: 2 bytes a
 weight; int8: a byte a weight plus a 4-byte scale per output row; int4 g128:
 half a byte a weight plus a 2-byte scale and a 2-byte zero per group of 128
-inputs; a tied LM head reads the bf16 embedding table)."""
+inputs; a tied LM head reads the bf16 embedding table); and the HBM traffic
+per launch computed from rocprofv3 counter tables (synthetic ones here)."""
+import json
 import os
 import subprocess
 import sys
@@ -67,3 +69,39 @@ def test_weight_bytes_per_token_of_the_quantised_workloads():
     assert round(got["8b"] / 1e9, 2) == 15.01
     assert round(got["8b_int8"] / 1e9, 2) == 7.51
     assert round(got["8b_int4"] / 1e9, 2) == 3.99
+
+
+def _counter_csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (kernel, counter, value) in enumerate(rows):
+            f.write(f'{i},"{kernel}",{counter},{value}\n')
+
+
+def test_traffic_from_counters(tmp_path, monkeypatch):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch):
+    the median over the decode kernel's dispatches, the near-empty
+    empty-queue launches left out, each counter scaled by the known bytes of
+    a device copy over what the same counter reads for it; a stored summary
+    is used only while the kernel source is the one it was taken on."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    k = "void amk::amk_vm<8, 0, false>(amk::VmParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    kib = bench.COPY_BYTES / 1024.0
+    _counter_csv(tmp_path / "f.csv", [(k, "FETCH_SIZE", 1000.0), (k, "FETCH_SIZE", 1010.0), (k, "FETCH_SIZE", 990.0),
+                                      (k, "FETCH_SIZE", 5.0), ("other_kernel", "FETCH_SIZE", 1e6)])
+    _counter_csv(tmp_path / "w.csv", [(k, "WRITE_SIZE", 100.0), (k, "WRITE_SIZE", 101.0), (k, "WRITE_SIZE", 100.0),
+                                      (k, "WRITE_SIZE", 0.1)])
+    _counter_csv(tmp_path / "cf.csv", [(copy, "FETCH_SIZE", kib * 1.05)] * 5)
+    _counter_csv(tmp_path / "cw.csv", [(copy, "WRITE_SIZE", kib * 0.98)] * 5)
+    out = bench.traffic_from("unit", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                             str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"))
+    want = 1000.0 * 1024 / 1.05 + 100.0 * 1024 / 0.98
+    assert out["dispatches"]["kernel_fetch"] == 3 and out["dispatches"]["kernel_write"] == 3
+    assert out["bytes_per_launch"] == pytest.approx(want, rel=1e-12)
+    assert bench.load_traffic("unit", 0) == pytest.approx(want, rel=1e-12)
+    stale = json.loads((tmp_path / "traffic_amk_vm_unit.json").read_text())
+    stale["kernel_sha256_16"] = "0" * 16
+    (tmp_path / "traffic_amk_vm_unit.json").write_text(json.dumps(stale))
+    assert bench.load_traffic("unit", 0) is None
+    assert bench.load_traffic("absent", 0) is None
